@@ -1,0 +1,178 @@
+"""Benchmark of the fused chunked sparse-KL loss head on one MI355X.
+
+One step = one forward call (teacher preparation, chunked fused GEMM with the
+online log-sum-exp and gather, sparse-KL reduction, loss) plus one backward
+call (teacher preparation, per chunk: logit recompute forming G, dH = G W,
+dW += G^T H), with dW zeroed at the start of each step.  Inputs are the
+32K-token large-vocabulary workload (T=32768, d=2880, V=201088, K=100, bf16,
+5% of positions masked), generated with the seeded recipe of
+chunked_sparse_kl_amd.synth and resident in device memory before timing.
+
+Prints ONE JSON line on stdout.  Progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+METRIC = "fused chunked KL fwd+bwd tokens/s & TFLOP/s (% bf16 MFMA peak); peak GiB"
+BF16_PEAK_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 dense bf16 flop/clk/CU
+HBM_PEAK_GBS = 8000.0
+WORKLOAD = 4                # 32K tokens, d=2880, V=201088, K=100
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source (otherwise None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = open(os.path.join(ROOT, "chunked_sparse_kl_amd", "csrc", rec["source_file"]), "rb").read()
+    if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+        return None
+    return rec["hbm_bytes_per_launch"]
+
+
+def cpu_baseline(inp: dict, rows: int, seed: int = 3) -> dict:
+    """The CPU fp64 oracle, as it stands, on a seeded subset of rows (forward and
+    backward of those rows)."""
+    from oracle import kl_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    n = inp["H"].shape[0]
+    S = np.sort(np.random.default_rng(seed).choice(n, size=rows, replace=False))
+    mask = inp["mask"].numpy()
+    t0 = time.perf_counter()
+    f = O.forward(inp["H"], inp["W"], inp["idx"].numpy(), inp["logp"], mask, rows=S)
+    b = O.backward(inp["H"], inp["W"], inp["idx"].numpy(), inp["logp"], mask, rows=S)
+    dt = time.perf_counter() - t0
+    assert np.isfinite(f["loss"]) and np.isfinite(b["dW"]).all()
+    return {"value": rows / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{rows} seeded rows of the same workload, forward + backward, fp64, "
+                      f"{dt:.1f} s wall"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--cpu-rows", type=int, default=64, help="rows of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: the loss head is measured on a single MI355X "
+              "(see the sharding notes in DESIGN.md); --gpus must be 1", file=sys.stderr)
+        return 2
+
+    import torch
+    import chunked_sparse_kl_amd as kd
+    from chunked_sparse_kl_amd import synth
+
+    dev = torch.device("cuda", 0)
+    w = synth.WORKLOADS[WORKLOAD]
+    log(f"generating inputs: {w.name}")
+    inp = synth.make_inputs(WORKLOAD)
+    H, W = inp["H"].to(dev), inp["W"].to(dev)
+    idx, logp, mask = inp["idx"].to(dev), inp["logp"].to(dev), inp["mask"].to(dev)
+    T, d, V, K = w.T, w.d, w.V, w.K
+    plan = kd.kd_plan_query(kd.KD_BF16, T, d, V, K, args.chunk)
+    log(f"plan: {plan}")
+    ws = torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device=dev)
+    dW = torch.empty((V, d), dtype=torch.float32, device=dev)
+    grad = torch.ones(1, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        fw = kd.kd_fused_chunked_kl_fwd(H, W, idx, logp, mask, workspace=ws, row_kl=False, plan=plan)
+        dW.zero_()
+        dH, _ = kd.kd_fused_chunked_kl_bwd(H, W, idx, logp, mask, fw["lse"], grad, workspace=ws,
+                                           dW=dW, plan=plan)
+        return fw["loss"], dH
+
+    for i in range(args.warmup):
+        loss, _ = step()
+        torch.cuda.synchronize()
+        log(f"warmup {i + 1}/{args.warmup} loss={loss.item():.6f}")
+    torch.cuda.reset_peak_memory_stats(dev)
+    kd.kd_profile_reset()
+    kd.kd_profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        loss, dH = step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kd.kd_profile_enable(False)
+    stats = kd.kd_profile_read()
+    peak_gib = torch.cuda.max_memory_allocated(dev) / 2**30
+    loss_v = loss.item()
+    log(f"timed {args.steps} steps in {elapsed:.3f} s, loss={loss_v:.6f}")
+
+    ms = elapsed / args.steps * 1e3
+    tokens_s = T * args.steps / elapsed
+    flop_step = 8.0 * T * d * V
+    tflops = flop_step / (ms * 1e-3) / 1e12
+    kernels = sorted(stats, key=lambda s: -s["total_ms"])
+    for s in kernels:
+        log(f"  {s['name']:16s} launches={s['launches']:4d} total={s['total_ms']:9.3f} ms "
+            f"avg={s['total_ms'] / s['launches']:8.3f} ms "
+            f"{(s['flops'] / (s['total_ms'] * 1e-3) / 1e12) if s['flops'] else 0:8.1f} TFLOP/s")
+    dom = kernels[0]
+    avg_ms = dom["total_ms"] / dom["launches"]
+    if dom["flops"] > 0:
+        achieved = dom["flops"] / dom["launches"] / (avg_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
+    else:
+        achieved = dom["bytes"] / dom["launches"] / (avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof["traffic"] = kernel_traffic(dom["name"])
+    roof["kernel"] = dom["name"]
+    roof["avg_launch_ms"] = round(avg_ms, 4)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on {args.cpu_rows} rows")
+        cpu = cpu_baseline(inp, args.cpu_rows)
+        log(f"cpu baseline: {cpu}")
+
+    props = torch.cuda.get_device_properties(dev)
+    out = {
+        "metric": METRIC, "value": round(tokens_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": T, "d": d, "V": V, "K": K, "mask": w.mask,
+                   "chunk": plan["chunk"], "n_chunks": plan["n_chunks"],
+                   "parallelism": "single GPU"},
+        "tflops": round(tflops, 1), "pct_bf16_peak": round(100 * tflops / BF16_PEAK_TFLOPS, 2),
+        "peak_gib": round(peak_gib, 3), "loss": loss_v,
+        "device": {"name": props.name, "compute_units": props.multi_processor_count},
+        "kernels": {s["name"]: {"launches": s["launches"], "total_ms": round(s["total_ms"], 3)}
+                    for s in kernels},
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

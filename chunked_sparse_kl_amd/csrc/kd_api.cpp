@@ -1,0 +1,508 @@
+// kdloss C ABI: argument validation, the chunk / workspace planner, the
+// per-chunk orchestration of the HIP kernels, and optional kernel timing.
+#include "../../include/kdloss.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kd_internal.h"
+
+namespace {
+
+using kd::DType;
+
+thread_local std::string g_last_error;
+std::atomic<int> g_validate{0};
+
+struct ValidateInit {
+  ValidateInit() {
+    const char* e = std::getenv("KDLOSS_VALIDATE");
+    if (e != nullptr && e[0] == '1') g_validate = 1;
+  }
+} g_validate_init;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return KD_OK;
+}
+
+// ------------------------------------------------------------------ timing
+struct Record {
+  const char* name;
+  hipEvent_t a, b;
+  double flops, bytes;
+};
+bool g_profile = false;
+std::vector<Record> g_records;
+struct Agg {
+  std::string name;
+  int64_t launches = 0;
+  double ms = 0, flops = 0, bytes = 0;
+};
+std::vector<Agg> g_agg;
+
+struct Timed {
+  Record r{};
+  hipStream_t s;
+  bool on;
+  Timed(hipStream_t st, const char* name, double flops, double bytes) : s(st), on(g_profile) {
+    if (!on) return;
+    r.name = name;
+    r.flops = flops;
+    r.bytes = bytes;
+    if (hipEventCreate(&r.a) != hipSuccess || hipEventCreate(&r.b) != hipSuccess) {
+      on = false;
+      return;
+    }
+    (void)hipEventRecord(r.a, s);
+  }
+  ~Timed() {
+    if (!on) return;
+    (void)hipEventRecord(r.b, s);
+    g_records.push_back(r);
+  }
+};
+
+void drain_records() {
+  for (Record& r : g_records) {
+    float ms = 0.f;
+    (void)hipEventSynchronize(r.b);
+    (void)hipEventElapsedTime(&ms, r.a, r.b);
+    auto it = std::find_if(g_agg.begin(), g_agg.end(), [&](const Agg& a) { return a.name == r.name; });
+    if (it == g_agg.end()) {
+      g_agg.push_back(Agg{});
+      it = g_agg.end() - 1;
+      it->name = r.name;
+    }
+    it->launches += 1;
+    it->ms += ms;
+    it->flops += r.flops;
+    it->bytes += r.bytes;
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  g_records.clear();
+}
+
+int check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(KD_E_HIP, "%s: %s", what, hipGetErrorString(e));
+  return KD_OK;
+}
+
+#define KD_LAUNCH(name, flops, bytes, call)          \
+  do {                                               \
+    {                                                \
+      Timed _t(s, name, (double)(flops), (double)(bytes)); \
+      call;                                          \
+    }                                                \
+    int _rc = check_launch(name);                    \
+    if (_rc != KD_OK) return _rc;                    \
+  } while (0)
+
+// ------------------------------------------------------------------ planning
+constexpr size_t kAlign = 256;
+constexpr int64_t kMaxAutoChunk = 8192;
+constexpr size_t kWorkspaceCap = size_t(24) << 30;
+constexpr int kScanTile = 4096;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+struct Layout {
+  DType dt;
+  int64_t n, d, V, K, chunk, c_pad, v_pad, n_vt, n_rb, n_keys, splits, scan_tiles;
+  // byte offsets
+  size_t ctrl, p, S, E, counts, offs, cursor, scan_tmp, hits, common_end;
+  size_t part, g, rowkl, fwd_end;
+  size_t G, GT, WT, HT, dhpart, bwd_end;
+};
+
+int dh_splits(DType dt, int64_t c_pad, int64_t d, int64_t v_pad) {
+  const int64_t tiles = ((c_pad + 255) / 256) * ((d + kd::TILE_D - 1) / kd::TILE_D);
+  const int64_t bk = dt == DType::BF16 ? 64 : 32;
+  const int64_t kb_total = (v_pad + bk - 1) / bk;
+  int64_t s = (1024 + tiles - 1) / tiles;
+  s = std::min<int64_t>(s, 32);
+  s = std::min<int64_t>(s, std::max<int64_t>(1, kb_total / 16));
+  s = std::max<int64_t>(s, 1);
+  const int64_t kb_per = (kb_total + s - 1) / s;
+  return (int)((kb_total + kb_per - 1) / kb_per);
+}
+
+Layout make_layout(DType dt, int64_t n, int64_t d, int64_t V, int64_t K, int64_t chunk) {
+  Layout L{};
+  L.dt = dt;
+  L.n = n;
+  L.d = d;
+  L.V = V;
+  L.K = K;
+  L.chunk = chunk;
+  L.c_pad = round_up(chunk, kd::KPAD);
+  L.v_pad = round_up(V, kd::KPAD);
+  L.n_vt = (V + kd::TILE_V - 1) / kd::TILE_V;
+  L.n_rb = (n + kd::ROW_BLOCK - 1) / kd::ROW_BLOCK;
+  L.n_keys = L.n_vt * L.n_rb;
+  L.splits = dh_splits(dt, L.c_pad, d, L.v_pad);
+  L.scan_tiles = (L.n_keys + kScanTile - 1) / kScanTile;
+  const size_t es = kd::elem_size(dt);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  L.ctrl = take(sizeof(kd::Ctrl));
+  L.p = take(size_t(n) * K * 4);
+  L.S = take(size_t(n) * 4);
+  L.E = take(size_t(n) * 4);
+  L.counts = take(size_t(L.n_keys) * 4);
+  L.offs = take(size_t(L.n_keys + 1) * 4);
+  L.cursor = take(size_t(L.n_keys) * 4);
+  L.scan_tmp = take(size_t(L.scan_tiles + 1) * 4);
+  L.hits = take(size_t(n) * K * 8);
+  L.common_end = o;
+  // forward-only region
+  L.part = take(size_t(L.n_vt) * chunk * 8);
+  L.g = take(size_t(n) * K * 4);
+  L.rowkl = take(size_t(n) * 4);
+  L.fwd_end = o;
+  // backward-only region (overlaps the forward-only one)
+  o = L.common_end;
+  L.G = take(size_t(L.c_pad) * L.v_pad * es);
+  L.GT = take(size_t(L.v_pad) * L.c_pad * es);
+  L.WT = take(size_t(d) * L.v_pad * es);
+  L.HT = take(size_t(d) * L.c_pad * es);
+  L.dhpart = take(size_t(L.splits) * L.c_pad * d * 4);
+  L.bwd_end = o;
+  return L;
+}
+
+int check_sizes(int dtype, int64_t n, int64_t d, int64_t V, int64_t K) {
+  if (dtype != KD_BF16 && dtype != KD_F32) return fail(KD_E_INVAL, "dtype %d is not KD_BF16 or KD_F32", dtype);
+  if (n <= 0 || d <= 0 || V <= 0 || K <= 0)
+    return fail(KD_E_INVAL, "sizes must be positive (n=%lld d=%lld V=%lld K=%lld)", (long long)n,
+                (long long)d, (long long)V, (long long)K);
+  if (K > V) return fail(KD_E_INVAL, "K=%lld exceeds V=%lld", (long long)K, (long long)V);
+  const int64_t epc = dtype == KD_BF16 ? 8 : 4;
+  if (d % epc != 0)
+    return fail(KD_E_INVAL, "d=%lld must be a multiple of %lld (16-byte rows)", (long long)d, (long long)epc);
+  const int64_t lim = (int64_t(1) << 31) - 1;
+  if (n > lim || V > lim - 4096 || d > lim || n * K > lim)
+    return fail(KD_E_INVAL, "sizes exceed the 32-bit index range of the kernels");
+  const int64_t n_keys = ((V + 255) / 256) * ((n + 63) / 64);
+  if ((n_keys + kScanTile - 1) / kScanTile > kScanTile)
+    return fail(KD_E_INVAL, "too many teacher-hit buckets (%lld)", (long long)n_keys);
+  return KD_OK;
+}
+
+int resolve_chunk(int64_t n, int64_t chunk, int64_t* out) {
+  if (chunk > 0) {
+    if (chunk >= n) {
+      *out = n;
+      return KD_OK;
+    }
+    if (chunk % kd::ROW_BLOCK != 0)
+      return fail(KD_E_INVAL, "chunk=%lld must be a multiple of %d (or >= n)", (long long)chunk,
+                  kd::ROW_BLOCK);
+    *out = chunk;
+    return KD_OK;
+  }
+  *out = 0;  // planner decides
+  return KD_OK;
+}
+
+int plan(int dtype, int64_t n, int64_t d, int64_t V, int64_t K, int64_t chunk, size_t budget_in,
+         Layout* out) {
+  int rc = check_sizes(dtype, n, d, V, K);
+  if (rc != KD_OK) return rc;
+  int64_t c = 0;
+  rc = resolve_chunk(n, chunk, &c);
+  if (rc != KD_OK) return rc;
+  const DType dt = static_cast<DType>(dtype);
+  if (c > 0) {
+    *out = make_layout(dt, n, d, V, K, c);
+    return KD_OK;
+  }
+  size_t budget = budget_in;
+  if (budget == 0) {
+    size_t free_b = 0, total_b = 0;
+    hipError_t e = hipMemGetInfo(&free_b, &total_b);
+    if (e != hipSuccess) return fail(KD_E_HIP, "hipMemGetInfo: %s", hipGetErrorString(e));
+    budget = free_b / 2;
+  }
+  budget = std::min(budget, kWorkspaceCap);
+  if (n <= 256) {
+    Layout L = make_layout(dt, n, d, V, K, n);
+    if (std::max(L.fwd_end, L.bwd_end) > budget)
+      return fail(KD_E_WORKSPACE, "workspace of %zu bytes exceeds the budget of %zu bytes",
+                  std::max(L.fwd_end, L.bwd_end), budget);
+    *out = L;
+    return KD_OK;
+  }
+  const int64_t half = round_up((n + 1) / 2, 256);
+  int64_t c_max = std::min<int64_t>(kMaxAutoChunk, std::max<int64_t>(256, half));
+  for (int64_t cand = c_max; cand >= 256; cand -= 256) {
+    const int64_t cc = std::min(cand, n);
+    Layout L = make_layout(dt, n, d, V, K, cc);
+    if (std::max(L.fwd_end, L.bwd_end) <= budget) {
+      *out = L;
+      return KD_OK;
+    }
+  }
+  Layout L = make_layout(dt, n, d, V, K, std::min<int64_t>(256, n));
+  return fail(KD_E_WORKSPACE, "no chunk size fits: the smallest plan (chunk 256) needs %zu bytes, budget %zu",
+              std::max(L.fwd_end, L.bwd_end), budget);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+int check_common(const void* H, const void* W, const int32_t* idx, const float* logp, void* ws,
+                 size_t ws_bytes, size_t need) {
+  if (H == nullptr || W == nullptr || idx == nullptr || logp == nullptr)
+    return fail(KD_E_INVAL, "H, W, topk_idx and topk_logp must be non-null");
+  if (!aligned16(H) || !aligned16(W)) return fail(KD_E_INVAL, "H and W must be 16-byte aligned");
+  if (ws == nullptr || ws_bytes < need)
+    return fail(KD_E_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, ws_bytes,
+                ws == nullptr ? " (null pointer)" : "");
+  if (!aligned16(ws)) return fail(KD_E_INVAL, "workspace must be 16-byte aligned");
+  return KD_OK;
+}
+
+// Teacher preparation and bucketing shared by both calls.
+int prepare_teacher(const Layout& L, const int32_t* idx, const float* logp, const uint8_t* mask,
+                    char* ws, hipStream_t s) {
+  auto* ctrl = reinterpret_cast<kd::Ctrl*>(ws + L.ctrl);
+  int* counts = reinterpret_cast<int*>(ws + L.counts);
+  const int n = (int)L.n, K = (int)L.K, V = (int)L.V;
+  const double nk = double(L.n) * L.K;
+  KD_LAUNCH("fill", 0, 0, kd::launch_fill_i32(reinterpret_cast<int*>(ctrl), 64, 0, s));
+  KD_LAUNCH("fill", 0, 0, kd::launch_fill_i32(counts, L.n_keys, 0, s));
+  KD_LAUNCH("teacher_prep", 0, nk * 12 + L.n * 9.0,
+            kd::launch_teacher_prep(logp, idx, mask, n, K, V, reinterpret_cast<float*>(ws + L.p),
+                                    reinterpret_cast<float*>(ws + L.S),
+                                    reinterpret_cast<float*>(ws + L.E), counts, (int)L.n_rb, ctrl, s));
+  if (g_validate.load()) {
+    kd::Ctrl host{};
+    hipError_t e = hipMemcpyAsync(&host, ctrl, sizeof(int) * 2, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return fail(KD_E_HIP, "validation read-back: %s", hipGetErrorString(e));
+    if (host.range_error)
+      return fail(KD_E_RANGE, "an unmasked row holds a teacher id outside [0, %d)", V);
+  }
+  KD_LAUNCH("hit_scan", 0, L.n_keys * 12.0,
+            kd::launch_scan(counts, (int)L.n_keys, reinterpret_cast<int*>(ws + L.offs),
+                            reinterpret_cast<int*>(ws + L.cursor),
+                            reinterpret_cast<int*>(ws + L.scan_tmp), s));
+  KD_LAUNCH("hit_scatter", 0, nk * 12,
+            kd::launch_hit_scatter(idx, mask, n, K, V, (int)L.n_rb,
+                                   reinterpret_cast<int*>(ws + L.cursor),
+                                   reinterpret_cast<int2*>(ws + L.hits), s));
+  return KD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kd_status_string(int status) {
+  switch (status) {
+    case KD_OK: return "KD_OK";
+    case KD_E_INVAL: return "KD_E_INVAL";
+    case KD_E_WORKSPACE: return "KD_E_WORKSPACE";
+    case KD_E_HIP: return "KD_E_HIP";
+    case KD_E_RANGE: return "KD_E_RANGE";
+    default: return "KD_UNKNOWN";
+  }
+}
+
+const char* kd_last_error_message(void) { return g_last_error.c_str(); }
+
+int kd_set_validate(int on) {
+  g_validate = on ? 1 : 0;
+  return ok();
+}
+
+int kd_profile_enable(int on) {
+  g_profile = on != 0;
+  return ok();
+}
+
+int kd_profile_reset(void) {
+  drain_records();
+  g_agg.clear();
+  return ok();
+}
+
+int kd_profile_read(kd_kernel_stat_t* out, int max_entries) {
+  drain_records();
+  if (out == nullptr) return (int)g_agg.size();
+  int m = std::min<int>(max_entries, (int)g_agg.size());
+  for (int i = 0; i < m; ++i) {
+    std::memset(&out[i], 0, sizeof(out[i]));
+    std::snprintf(out[i].name, sizeof(out[i].name), "%s", g_agg[i].name.c_str());
+    out[i].launches = g_agg[i].launches;
+    out[i].total_ms = g_agg[i].ms;
+    out[i].flops = g_agg[i].flops;
+    out[i].bytes = g_agg[i].bytes;
+  }
+  return m;
+}
+
+int kd_plan_query(int dtype, int64_t n, int64_t d, int64_t V, int32_t K, int64_t chunk,
+                  size_t hbm_budget, kd_plan_t* out) {
+  if (out == nullptr) return fail(KD_E_INVAL, "out must be non-null");
+  Layout L;
+  int rc = plan(dtype, n, d, V, K, chunk, hbm_budget, &L);
+  if (rc != KD_OK) return rc;
+  out->chunk = L.chunk;
+  out->n_chunks = (L.n + L.chunk - 1) / L.chunk;
+  out->vocab_tiles = L.n_vt;
+  out->dh_splits = L.splits;
+  out->fwd_workspace_bytes = L.fwd_end;
+  out->bwd_workspace_bytes = L.bwd_end;
+  out->workspace_bytes = std::max(L.fwd_end, L.bwd_end);
+  return ok();
+}
+
+int kd_fused_chunked_kl_fwd(int dtype, const void* H, const void* W, const int32_t* topk_idx,
+                            const float* topk_logp, const uint8_t* mask, int64_t n, int64_t d,
+                            int64_t V, int32_t K, int64_t chunk, void* workspace,
+                            size_t workspace_bytes, float* loss, float* lse, float* row_kl,
+                            float* gathered, void* stream) {
+  Layout L;
+  int rc = plan(dtype, n, d, V, K, chunk, workspace_bytes ? workspace_bytes : 1, &L);
+  if (rc != KD_OK && rc != KD_E_WORKSPACE) return rc;
+  if (rc == KD_E_WORKSPACE) {
+    // auto chunk with an undersized buffer: report what the smallest plan needs
+    return rc;
+  }
+  if (loss == nullptr || lse == nullptr) return fail(KD_E_INVAL, "loss and lse must be non-null");
+  rc = check_common(H, W, topk_idx, topk_logp, workspace, workspace_bytes, L.fwd_end);
+  if (rc != KD_OK) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  rc = prepare_teacher(L, topk_idx, topk_logp, mask, ws, s);
+  if (rc != KD_OK) return rc;
+
+  const size_t es = kd::elem_size(L.dt);
+  float* g = gathered != nullptr ? gathered : reinterpret_cast<float*>(ws + L.g);
+  float* rk = row_kl != nullptr ? row_kl : reinterpret_cast<float*>(ws + L.rowkl);
+  auto* part = reinterpret_cast<float2*>(ws + L.part);
+  for (int64_t c0 = 0; c0 < L.n; c0 += L.chunk) {
+    const int rows = (int)std::min<int64_t>(L.chunk, L.n - c0);
+    kd::FwdEpilogue ep{};
+    ep.part = part;
+    ep.ld_part = (int)L.chunk;
+    ep.n_vt = (int)L.n_vt;
+    ep.c0 = (int)c0;
+    ep.rows = rows;
+    ep.V = (int)L.V;
+    ep.K = (int)L.K;
+    ep.n_rb = (int)L.n_rb;
+    ep.hit_off = reinterpret_cast<const int*>(ws + L.offs);
+    ep.hits = reinterpret_cast<const int2*>(ws + L.hits);
+    ep.idx = topk_idx;
+    ep.g = g;
+    const char* Hc = static_cast<const char*>(H) + c0 * L.d * es;
+    const double fl = 2.0 * rows * L.d * L.V;
+    const double by = double(L.V) * L.d * es + double(rows) * L.d * es + double(rows) * L.n_vt * 8;
+    KD_LAUNCH("fwd_gemm", fl, by, kd::launch_fwd_gemm(L.dt, W, (int)L.V, Hc, rows, (int)L.d, ep, s));
+    KD_LAUNCH("lse_kl", 0, double(rows) * (L.n_vt * 8 + L.K * 8 + 16),
+              kd::launch_lse_kl(part, (int)L.chunk, (int)L.n_vt, (int)c0, rows,
+                                reinterpret_cast<const float*>(ws + L.p), g,
+                                reinterpret_cast<const float*>(ws + L.S),
+                                reinterpret_cast<const float*>(ws + L.E), mask, (int)L.K, lse, rk, s));
+  }
+  KD_LAUNCH("loss", 0, L.n * 4.0,
+            kd::launch_loss(rk, (int)L.n, reinterpret_cast<const kd::Ctrl*>(ws + L.ctrl), loss, s));
+  return ok();
+}
+
+int kd_fused_chunked_kl_bwd(int dtype, const void* H, const void* W, const int32_t* topk_idx,
+                            const float* topk_logp, const uint8_t* mask, int64_t n, int64_t d,
+                            int64_t V, int32_t K, int64_t chunk, const float* lse,
+                            const float* grad_loss, void* dH, float* dW, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  Layout L;
+  int rc = plan(dtype, n, d, V, K, chunk, workspace_bytes ? workspace_bytes : 1, &L);
+  if (rc != KD_OK) return rc;
+  if (lse == nullptr || grad_loss == nullptr || dH == nullptr || dW == nullptr)
+    return fail(KD_E_INVAL, "lse, grad_loss, dH and dW must be non-null");
+  if (!aligned16(dH) || !aligned16(dW)) return fail(KD_E_INVAL, "dH and dW must be 16-byte aligned");
+  rc = check_common(H, W, topk_idx, topk_logp, workspace, workspace_bytes, L.bwd_end);
+  if (rc != KD_OK) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  rc = prepare_teacher(L, topk_idx, topk_logp, mask, ws, s);
+  if (rc != KD_OK) return rc;
+
+  const size_t es = kd::elem_size(L.dt);
+  KD_LAUNCH("transpose_w", 0, 2.0 * L.V * L.d * es,
+            kd::launch_transpose_pad(L.dt, W, (int)L.V, (int)L.d, L.d, ws + L.WT, (int)L.v_pad,
+                                     L.v_pad, s));
+  for (int64_t c0 = 0; c0 < L.n; c0 += L.chunk) {
+    const int rows = (int)std::min<int64_t>(L.chunk, L.n - c0);
+    const int c_pad = (int)round_up(rows, kd::KPAD);
+    const char* Hc = static_cast<const char*>(H) + c0 * L.d * es;
+    KD_LAUNCH("transpose_h", 0, 2.0 * rows * L.d * es,
+              kd::launch_transpose_pad(L.dt, Hc, rows, (int)L.d, L.d, ws + L.HT, c_pad, c_pad, s));
+    kd::RecomputeEpilogue ep{};
+    ep.G = ws + L.G;
+    ep.GT = ws + L.GT;
+    ep.v_pad = (int)L.v_pad;
+    ep.c_pad = c_pad;
+    ep.c0 = (int)c0;
+    ep.rows = rows;
+    ep.V = (int)L.V;
+    ep.K = (int)L.K;
+    ep.n_rb = (int)L.n_rb;
+    ep.hit_off = reinterpret_cast<const int*>(ws + L.offs);
+    ep.hits = reinterpret_cast<const int2*>(ws + L.hits);
+    ep.idx = topk_idx;
+    ep.p = reinterpret_cast<const float*>(ws + L.p);
+    ep.S = reinterpret_cast<const float*>(ws + L.S);
+    ep.lse = lse;
+    ep.mask = mask;
+    ep.ctrl = reinterpret_cast<const kd::Ctrl*>(ws + L.ctrl);
+    ep.grad_loss = grad_loss;
+    const double fl = 2.0 * rows * L.d * L.V;
+    KD_LAUNCH("recompute_gemm", fl,
+              double(L.V) * L.d * es + double(rows) * L.d * es + 2.0 * c_pad * L.v_pad * es,
+              kd::launch_recompute_gemm(L.dt, W, (int)L.V, Hc, rows, (int)L.d, ep, s));
+    const long long split_stride = (long long)L.c_pad * L.d;
+    KD_LAUNCH("dh_gemm", fl,
+              double(c_pad) * L.v_pad * es + double(L.d) * L.v_pad * es + double(L.splits) * rows * L.d * 4,
+              kd::launch_dh_gemm(L.dt, ws + L.G, rows, (int)L.v_pad, ws + L.WT, (int)L.d,
+                                 (int)L.splits, reinterpret_cast<float*>(ws + L.dhpart),
+                                 split_stride, s));
+    KD_LAUNCH("dh_reduce", 0, double(L.splits) * rows * L.d * 4 + double(rows) * L.d * es,
+              kd::launch_dh_reduce(L.dt, reinterpret_cast<const float*>(ws + L.dhpart),
+                                   (int)L.splits, split_stride, rows, (int)L.d,
+                                   static_cast<char*>(dH) + c0 * L.d * es, s));
+    KD_LAUNCH("dw_gemm", fl,
+              double(L.V) * c_pad * es + double(L.d) * c_pad * es + 2.0 * L.V * L.d * 4,
+              kd::launch_dw_gemm(L.dt, ws + L.GT, (int)L.V, c_pad, ws + L.HT, (int)L.d, dW, s));
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,100 @@
+// Internal declarations shared by the kdloss HIP sources: tile constants,
+// the device control block and the host-side kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace kd {
+
+// Fused GEMM tiling.  The vocabulary tile (TILE_V) and the row-block size
+// (ROW_BLOCK) also key the teacher-hit buckets, so every kernel that touches
+// those buckets must agree on them.
+constexpr int TILE_V = 256;     // vocabulary rows per fused-GEMM tile
+constexpr int TILE_T = 256;     // token columns per fused-GEMM tile
+constexpr int TILE_D = 192;     // hidden-dim columns per dH / dW tile (2880 = 15*192, 3072 = 16*192)
+constexpr int ROW_BLOCK = 64;   // chunk starts are multiples of this many rows
+constexpr int KPAD = 64;        // contraction lengths of dH / dW are padded to this
+
+// Written by the teacher-preparation kernel, read by later kernels.
+struct Ctrl {
+  int n_valid;       // number of unmasked rows
+  int range_error;   // 1 if an unmasked row had an id outside [0, V)
+  int pad[62];
+};
+
+enum class DType { BF16 = 0, F32 = 1 };
+
+inline size_t elem_size(DType t) { return t == DType::BF16 ? 2 : 4; }
+
+// ---------------------------------------------------------------- small kernels
+void launch_fill_i32(int* p, long long count, int value, hipStream_t s);
+void launch_teacher_prep(const float* logp, const int* idx, const uint8_t* mask, int n, int K, int V,
+                         float* p, float* S, float* E, int* counts, int n_rb, Ctrl* ctrl,
+                         hipStream_t s);
+void launch_scan(const int* counts, int n_keys, int* offsets, int* cursor, int* tmp, hipStream_t s);
+void launch_hit_scatter(const int* idx, const uint8_t* mask, int n, int K, int V, int n_rb,
+                        int* cursor, int2* hits, hipStream_t s);
+void launch_lse_kl(const float2* part, int ld_part, int n_vt, int c0, int rows, const float* p,
+                   const float* g, const float* S, const float* E, const uint8_t* mask, int K,
+                   float* lse, float* row_kl, hipStream_t s);
+void launch_loss(const float* row_kl, int n, const Ctrl* ctrl, float* loss, hipStream_t s);
+void launch_transpose_pad(DType t, const void* in, int rows, int cols, long long ld_in, void* out,
+                          int rows_pad, long long ld_out, hipStream_t s);
+void launch_dh_reduce(DType t, const float* part, int splits, long long split_stride, int rows,
+                      int d, void* dH, hipStream_t s);
+
+// ---------------------------------------------------------------- GEMMs
+struct FwdEpilogue {
+  float2* part;        // [n_vt][ld_part] (max, sum-exp) per vocab tile and chunk row
+  int ld_part;
+  int n_vt;
+  int c0;              // global row of the chunk start
+  int rows;            // rows in this chunk
+  int V;
+  int K;
+  int n_rb;
+  const int* hit_off;  // [n_vt * n_rb + 1]
+  const int2* hits;    // (row, k) sorted by (vocab tile, row block)
+  const int* idx;      // [n, K]
+  float* g;            // [n, K] gathered logits
+};
+
+struct RecomputeEpilogue {
+  void* G;             // [c_pad][v_pad] dtype
+  void* GT;            // [v_pad][c_pad] dtype
+  int v_pad;
+  int c_pad;
+  int c0;
+  int rows;
+  int V;
+  int K;
+  int n_rb;
+  const int* hit_off;
+  const int2* hits;
+  const int* idx;
+  const float* p;      // [n, K] renormalised teacher probabilities
+  const float* S;      // [n]
+  const float* lse;    // [n]
+  const uint8_t* mask; // [n] or null
+  const Ctrl* ctrl;
+  const float* grad_loss;
+};
+
+// Z = W * H_c^T over one chunk (vocab rows x chunk tokens), epilogue: per
+// (token, vocab tile) max / sum-exp partials and the gather at teacher ids.
+void launch_fwd_gemm(DType t, const void* W, int V, const void* Hc, int rows, int d,
+                     const FwdEpilogue& ep, hipStream_t s);
+// Same contraction, epilogue: G = grad * w_t (S_t q - scatter p) into G and G^T.
+void launch_recompute_gemm(DType t, const void* W, int V, const void* Hc, int rows, int d,
+                           const RecomputeEpilogue& ep, hipStream_t s);
+// part[split][c_pad][d] = G[:, split range] * W^T[split range, :]  (fp32 partials)
+void launch_dh_gemm(DType t, const void* G, int rows, int v_pad, const void* WT, int d,
+                    int splits, float* part, long long split_stride, hipStream_t s);
+// dW[V][d] += G^T * H_c
+void launch_dw_gemm(DType t, const void* GT, int V, int c_pad, const void* HT, int d, float* dW,
+                    hipStream_t s);
+
+}  // namespace kd

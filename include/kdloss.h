@@ -1,0 +1,162 @@
+/*
+ * kdloss — fused, chunked sparse-KL distillation loss head for AMD Instinct
+ * MI355X (gfx950).  C ABI: plain pointers and sizes only.
+ *
+ * The operation (Hugging Face blog "Making Knowledge Distillation Cheap Enough
+ * to Run at Scale", section "Two systems changes"; arXiv 2608.03796 abstract;
+ * aib.vote summary, paragraph comparing Dense, Forward-chunked and Fused
+ * chunked KL): the student's output projection (logits z = H W^T over the
+ * whole vocabulary) is fused with a full-vocabulary log-softmax and a KL
+ * divergence against the teacher's cached top-K entries (the offline top-K
+ * cache of that same section).  Rows are processed one chunk at a time; the
+ * n x V logit matrix is never stored, and the backward call recomputes each
+ * chunk's logits (the "fused chunked" variant), so device memory grows
+ * linearly with n.
+ *
+ * Definition computed, per row t with teacher ids i_{t,k}, values a_{t,k}:
+ *   log q_{t,v} = z_{t,v} - LSE_v(z_t)                 (full vocabulary)
+ *   l_{t,k} = a_{t,k} - LSE_k(a_t),  p_{t,k} = exp(l)  (teacher renormalised over K)
+ *   KL_t    = sum_k p_{t,k} (l_{t,k} - log q_{t,i_{t,k}})
+ *   loss    = sum_{t: mask_t != 0} KL_t / N_valid       (0 if N_valid == 0)
+ * and its gradient (the closed form the blog refers to in its closing
+ * paragraph):  G_{t,v} = grad_loss * [mask_t] / N_valid * (S_t q_{t,v} -
+ * sum_k p_{t,k} [i_{t,k} = v]),  S_t = sum_k p_{t,k};  dH = G W,  dW += G^T H.
+ * No tail bucket: the teacher's mass lives only on its K ids; temperature 1.
+ *
+ * Layouts (all row-major, contiguous):
+ *   H        [n, d]  dtype (bf16 or fp32)        student hidden states
+ *   W        [V, d]  dtype                       output-projection weight
+ *   topk_idx [n, K]  int32 in [0, V)             teacher ids (duplicates allowed: summed)
+ *   topk_logp[n, K]  fp32                        teacher log-values (any per-row offset;
+ *                                                -inf = zero probability)
+ *   mask     [n]     uint8, NULL = all ones      0 removes the row entirely (its ids
+ *                                                and values are never read)
+ * All device pointers are allocated and owned by the caller; H, W, dH and dW
+ * must be 16-byte aligned and d must be a multiple of 8 (bf16) or 4 (fp32).
+ * Calls are asynchronous on `stream` (a hipStream_t; NULL = default stream)
+ * and never synchronise the host, except when validation is switched on.
+ * No C++ exception crosses this interface.  NaN / Inf in inputs propagate to
+ * the outputs and are not reported as errors.
+ */
+#ifndef KDLOSS_H
+#define KDLOSS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types of H, W and dH (H and W share one). */
+enum { KD_BF16 = 0, KD_F32 = 1 };
+
+/* Status codes returned by every call. */
+enum {
+  KD_OK = 0,
+  KD_E_INVAL = -1,     /* null pointer, size <= 0, K > V, misalignment, bad dtype or chunk */
+  KD_E_WORKSPACE = -2, /* workspace too small (the message gives the bytes needed) or no plan fits */
+  KD_E_HIP = -3,       /* a HIP runtime call or kernel launch failed */
+  KD_E_RANGE = -4      /* a teacher id outside [0, V) on an unmasked row (validation mode only) */
+};
+
+/* Result of the chunk and workspace planner. */
+typedef struct kd_plan {
+  int64_t chunk;               /* rows per chunk (the last chunk may be shorter) */
+  int64_t n_chunks;
+  int64_t vocab_tiles;         /* 256-wide vocabulary tiles of the fused GEMMs */
+  int64_t dh_splits;           /* split-K factor of the dH = G W contraction */
+  size_t fwd_workspace_bytes;  /* needed by kd_fused_chunked_kl_fwd */
+  size_t bwd_workspace_bytes;  /* needed by kd_fused_chunked_kl_bwd */
+  size_t workspace_bytes;      /* max of the two: one buffer can serve both calls */
+} kd_plan_t;
+
+/*
+ * Chooses the chunk size and reports the workspace each call needs.  The
+ * chunk bounds the only per-chunk buffers (the bf16/fp32 logit-gradient
+ * slices G and G^T of chunk x V entries); everything else is linear in n.
+ * chunk > 0 is honoured as given (it must be a multiple of 64 unless it is
+ * >= n).  chunk <= 0 lets the planner pick the largest multiple of 256 that is
+ * <= 8192, <= max(256, n/2 rounded up to 256) and whose workspace fits in
+ * min(hbm_budget, 24 GiB).  hbm_budget == 0 means: half of the device's free
+ * memory (hipMemGetInfo on the current device); otherwise no device call is
+ * made.  The same (dtype, n, d, V, K, chunk) always yields the same plan for
+ * the same budget.
+ */
+int kd_plan_query(int dtype, int64_t n, int64_t d, int64_t V, int32_t K, int64_t chunk,
+                  size_t hbm_budget, kd_plan_t* out);
+
+/*
+ * Forward: loss, per-row log-sum-exp and per-row KL.
+ *   loss     [1] fp32 device, written (mean KL over unmasked rows)
+ *   lse      [n] fp32 device, written: LSE over the full vocabulary of each
+ *            row's logits (also for masked rows); pass it unchanged to bwd
+ *   row_kl   [n] fp32 device or NULL: KL_t (0 for masked rows)
+ *   gathered [n, K] fp32 device or NULL: z_{t, i_{t,k}}, the student logit at
+ *            each teacher id, taken from the same GEMM tiles that feed the
+ *            log-sum-exp (undefined on masked rows)
+ *   workspace: device buffer of at least plan.fwd_workspace_bytes for the same
+ *            (dtype, n, d, V, K, chunk); its contents need not be initialised.
+ * The result does not depend on the chunk size (bitwise, for loss and lse).
+ */
+int kd_fused_chunked_kl_fwd(int dtype, const void* H, const void* W, const int32_t* topk_idx,
+                            const float* topk_logp, const uint8_t* mask, int64_t n, int64_t d,
+                            int64_t V, int32_t K, int64_t chunk, void* workspace,
+                            size_t workspace_bytes, float* loss, float* lse, float* row_kl,
+                            float* gathered, void* stream);
+
+/*
+ * Backward: recomputes each chunk's logits from H and W, forms G in registers
+ * (rounded to the input dtype), then dH = G W and dW += G^T H.
+ *   lse       [n] fp32 device: exactly what kd_fused_chunked_kl_fwd wrote
+ *   grad_loss [1] fp32 device: upstream gradient of the loss (1 for plain training)
+ *   dH        [n, d] dtype device: OVERWRITTEN (rows of masked positions are 0)
+ *   dW        [V, d] fp32 device: ACCUMULATED (+=); the caller zeroes it first
+ *   workspace: at least plan.bwd_workspace_bytes.
+ * No gradient is produced for the teacher inputs.
+ */
+int kd_fused_chunked_kl_bwd(int dtype, const void* H, const void* W, const int32_t* topk_idx,
+                            const float* topk_logp, const uint8_t* mask, int64_t n, int64_t d,
+                            int64_t V, int32_t K, int64_t chunk, const float* lse,
+                            const float* grad_loss, void* dH, float* dW, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* kd_status_string(int status);
+
+/* Message of the last failing call on this host thread ("" if none). */
+const char* kd_last_error_message(void);
+
+/*
+ * Validation mode (off by default; the environment variable KDLOSS_VALIDATE=1
+ * switches it on at load time).  When on, fwd and bwd synchronise the stream
+ * after teacher preparation and return KD_E_RANGE if an unmasked row holds an
+ * id outside [0, V).  When off such ids are skipped (their terms are missing
+ * and gathered values are left unwritten) but never read out of bounds.
+ */
+int kd_set_validate(int on);
+
+/*
+ * Kernel timing.  While enabled, every kernel launch is bracketed by two HIP
+ * events recorded on the call's stream; kd_profile_read synchronises on the
+ * recorded events and returns, per kernel class, the launch count, the summed
+ * event-to-event time, and the algorithmic flops and bytes of those launches.
+ * The records are kept per process and are not thread-safe.
+ */
+typedef struct kd_kernel_stat {
+  char name[48];
+  int64_t launches;
+  double total_ms;
+  double flops;   /* algorithmic: 2*M*N*K for the contractions, 0 otherwise */
+  double bytes;   /* algorithmic HBM bytes (operands read once, outputs written once) */
+} kd_kernel_stat_t;
+
+int kd_profile_enable(int on);
+int kd_profile_reset(void);
+int kd_profile_read(kd_kernel_stat_t* out, int max_entries);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDLOSS_H */

@@ -1,0 +1,116 @@
+"""Host-side checks of the C ABI: the library loads, exports what include/kdloss.h
+declares, the planner behaves as documented, and bad arguments are rejected
+before any device work (no kernel is launched in these tests)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import chunked_sparse_kl_amd as kd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kdloss.h")
+GiB = 1 << 30
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built_library():
+    if not os.path.exists(kd.library_path()):
+        from chunked_sparse_kl_amd import build
+        build.build()
+    return kd.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kd_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_symbols():
+    assert _declared_functions() == sorted(kd.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", kd.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\b[TW] (kd_[a-z_]+)$", out, flags=re.M))
+    for name in _declared_functions():
+        assert name in exported, name
+        assert hasattr(kd.lib(), name)
+
+
+def test_status_strings():
+    lib = kd.lib()
+    for code, name in [(0, b"KD_OK"), (-1, b"KD_E_INVAL"), (-2, b"KD_E_WORKSPACE"), (-3, b"KD_E_HIP"),
+                       (-4, b"KD_E_RANGE")]:
+        assert lib.kd_status_string(code) == name
+
+
+@pytest.mark.parametrize("n,d,V,want", [
+    (4096, 3072, 128256, 2048),      # toy head, 4K tokens
+    (8192, 3072, 128256, 4096),      # packed 8K
+    (32768, 2880, 201088, 8192),     # 32K, large vocabulary
+    (262144, 3072, 128256, 8192),    # 256K
+    (256, 256, 4096, 256),           # small: a single chunk
+    (300, 256, 4096, 256),
+])
+def test_planner_default_chunks(n, d, V, want):
+    p = kd.kd_plan_query(kd.KD_BF16, n, d, V, 100, 0, 200 * GiB)
+    assert p["chunk"] == want
+    assert p["n_chunks"] == -(-n // want)
+    assert p["workspace_bytes"] == max(p["fwd_workspace_bytes"], p["bwd_workspace_bytes"])
+
+
+def test_planner_respects_budget_and_explicit_chunk():
+    big = kd.kd_plan_query(kd.KD_BF16, 32768, 2880, 201088, 100, 0, 200 * GiB)
+    small = kd.kd_plan_query(kd.KD_BF16, 32768, 2880, 201088, 100, 0, big["workspace_bytes"] // 3)
+    assert small["chunk"] < big["chunk"] and small["chunk"] % 256 == 0
+    assert small["workspace_bytes"] <= big["workspace_bytes"] // 3
+    # a buffer of exactly the planned size yields the same plan (fwd/bwd use that rule)
+    same = kd.kd_plan_query(kd.KD_BF16, 32768, 2880, 201088, 100, 0, big["workspace_bytes"])
+    assert same == big
+    expl = kd.kd_plan_query(kd.KD_F32, 256, 256, 4096, 16, 64, 0)
+    assert expl["chunk"] == 64 and expl["n_chunks"] == 4
+    with pytest.raises(kd.KdError) as e:
+        kd.kd_plan_query(kd.KD_BF16, 32768, 2880, 201088, 100, 0, 1 << 20)
+    assert e.value.status == -2
+
+
+def test_workspace_is_linear_in_rows():
+    # fixed chunk: every buffer other than the per-chunk ones scales with n
+    sizes = [kd.kd_plan_query(kd.KD_BF16, n, 3072, 128256, 100, 8192, 0)["workspace_bytes"]
+             for n in (16384, 32768, 65536, 131072, 262144)]
+    slopes = [(b - a) / (m - k) for a, b, k, m in zip(sizes, sizes[1:], (16384, 32768, 65536, 131072),
+                                                        (32768, 65536, 131072, 262144))]
+    assert max(slopes) - min(slopes) <= 0.01 * max(slopes)
+    assert max(slopes) < 4096  # bytes per row: teacher buffers only, never a vocabulary-sized row
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(dtype=2), -1), (dict(n=0), -1), (dict(K=5000), -1), (dict(d=250), -1), (dict(chunk=100), -1),
+])
+def test_bad_sizes_rejected(kwargs, code):
+    args = dict(dtype=kd.KD_BF16, n=1000, d=256, V=4096, K=16, chunk=0)
+    args.update(kwargs)
+    with pytest.raises(kd.KdError) as e:
+        kd.kd_plan_query(args["dtype"], args["n"], args["d"], args["V"], args["K"], args["chunk"], GiB)
+    assert e.value.status == code
+
+
+def test_null_pointers_rejected_without_device_work():
+    lib = kd.lib()
+    loss = ctypes.c_void_p(16)
+    rc = lib.kd_fused_chunked_kl_fwd(0, None, None, None, None, None, 256, 256, 4096, 16, 64, None, 0,
+                                     loss, loss, None, None, None)
+    assert rc == -1 and b"non-null" in lib.kd_last_error_message()
+    fake = ctypes.c_void_p(4096)
+    rc = lib.kd_fused_chunked_kl_fwd(0, fake, fake, fake, fake, None, 256, 256, 4096, 16, 64, None, 0,
+                                     fake, fake, None, None, None)
+    assert rc == -2 and b"workspace" in lib.kd_last_error_message()
+    misaligned = ctypes.c_void_p(4104)
+    rc = lib.kd_fused_chunked_kl_bwd(0, misaligned, fake, fake, fake, None, 256, 256, 4096, 16, 64,
+                                     fake, fake, fake, fake, fake, 1 << 30, None)
+    assert rc == -1 and b"aligned" in lib.kd_last_error_message()

@@ -1,0 +1,199 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU fp64 oracle.
+
+Small cases are compared element by element over every row; they are sized
+to span several 256-row / 256-vocabulary tiles, a ragged vocabulary tile, a
+ragged K (hidden-dim) block and a ragged last chunk.  The five workloads are
+checked at full size on a seeded row subset (per-row values on the subset in
+the run as given; loss, dH and dW in a second run whose mask keeps only the
+subset), in the chunking the benchmark uses.
+"""
+import numpy as np
+import pytest
+import torch
+
+import chunked_sparse_kl_amd as kd
+from chunked_sparse_kl_amd import synth
+from oracle import kl_oracle as O
+from tests.parity_util import check_full, check_subset, rel_fro, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(autouse=True)
+def _name(request):
+    _log(f"[case] {request.node.name}")
+    yield
+
+
+# ------------------------------------------------------------------ small, full comparison
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("chunk", [256, 448, 0])
+def test_small_ragged(dtype, chunk):
+    inp = synth.make_custom(700, 200, 1000, 20, dtype, "random5", "uniform", seed=11)
+    gpu = run_gpu(inp, chunk=chunk)
+    check_full(inp, gpu, dtype)
+
+
+def test_tiny_fp32_workload_full():
+    inp = synth.make_inputs(1)
+    gpu = run_gpu(inp, chunk=inp["workload"].chunk)
+    assert gpu["plan"]["chunk"] == 64
+    check_full(inp, gpu, "f32")
+
+
+@pytest.mark.parametrize("n", [1, 63, 65])
+def test_few_rows(n):
+    inp = synth.make_custom(n, 64, 777, 5, "bf16", "ones", "uniform", seed=3)
+    check_full(inp, run_gpu(inp), "bf16")
+
+
+def test_k_equals_v_and_k_one():
+    inp = synth.make_custom(96, 64, 320, 320, "bf16", "random5", "uniform", seed=4)
+    check_full(inp, run_gpu(inp, chunk=64), "bf16")
+    inp = synth.make_custom(96, 64, 320, 1, "bf16", "random5", "uniform", seed=5)
+    check_full(inp, run_gpu(inp, chunk=64), "bf16")
+
+
+def test_duplicates_neginf_and_shifted_teacher():
+    inp = synth.make_custom(300, 128, 900, 12, "bf16", "random5", "uniform", seed=6)
+    inp["idx"][3, 1] = inp["idx"][3, 0]            # duplicate id within a row: summed
+    inp["idx"][7, 2:5] = inp["idx"][7, 1]
+    inp["logp"][10, -1] = float("-inf")            # zero-probability entry
+    inp["logp"] += torch.randn(300, 1) * 5.0       # raw logits, not log-probs: renormalised over K
+    gpu = run_gpu(inp, chunk=128, grad=0.37)
+    check_full(inp, gpu, "bf16", grad=0.37)
+
+
+def test_clustered_ids_overflow_tiles():
+    # every teacher id of every row inside one 256-wide vocabulary tile
+    inp = synth.make_custom(256, 64, 2048, 100, "bf16", "ones", "uniform", seed=8)
+    rng = np.random.default_rng(0)
+    inp["idx"] = torch.from_numpy(np.stack([rng.permutation(256)[:100] + 512 for _ in range(256)]).astype(np.int32))
+    check_full(inp, run_gpu(inp, chunk=128), "bf16")
+
+
+# ------------------------------------------------------------------ semantics
+def test_all_masked_rows_give_zero():
+    inp = synth.make_custom(200, 64, 500, 8, "bf16", "ones", "uniform", seed=9)
+    inp["mask"][:] = 0
+    gpu = run_gpu(inp, chunk=64)
+    assert gpu["loss"] == 0.0
+    assert not gpu["dH"].any() and not gpu["dW"].any()
+    assert np.isfinite(gpu["lse"]).all()
+
+
+def test_masked_rows_never_read():
+    inp = synth.make_custom(256, 64, 700, 10, "bf16", "random5", "uniform", seed=10)
+    clean = run_gpu(inp, chunk=64)
+    dead = inp["mask"] == 0
+    inp["logp"][dead] = float("nan")
+    inp["idx"][dead] = -77777
+    dirty = run_gpu(inp, chunk=64)
+    assert dirty["loss"] == clean["loss"]
+    assert np.array_equal(dirty["dW"], clean["dW"]) and np.array_equal(dirty["dH"], clean["dH"])
+
+
+def test_chunk_size_independence_bitwise_loss():
+    inp = synth.make_custom(1000, 256, 3000, 16, "bf16", "random5", "uniform", seed=12)
+    ref = run_gpu(inp, chunk=1000)
+    live = inp["mask"].numpy() != 0  # gathered values are undefined on masked rows
+    for c in (64, 192, 256, 512, 0):
+        got = run_gpu(inp, chunk=c)
+        assert got["loss"] == ref["loss"], c
+        assert np.array_equal(got["lse"], ref["lse"]) and np.array_equal(got["row_kl"], ref["row_kl"])
+        assert np.array_equal(got["g"][live], ref["g"][live])
+        assert rel_fro(got["dW"], ref["dW"]) <= 1e-5 and rel_fro(got["dH"], ref["dH"]) <= 5e-3
+
+
+def test_deterministic_repeat():
+    inp = synth.make_custom(600, 256, 2000, 16, "bf16", "random5", "uniform", seed=13)
+    a = run_gpu(inp, chunk=256)
+    b = run_gpu(inp, chunk=256)
+    assert a["loss"] == b["loss"]
+    for k in ("lse", "row_kl", "g", "dH", "dW"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("chunk", [300, 128])
+def test_dw_accumulates_and_grad_scales(chunk):
+    inp = synth.make_custom(300, 64, 900, 12, "bf16", "random5", "uniform", seed=14)
+    d = {k: v.cuda() for k, v in inp.items() if torch.is_tensor(v)}
+    fw = kd.kd_fused_chunked_kl_fwd(d["H"], d["W"], d["idx"], d["logp"], d["mask"], chunk=chunk)
+    g = torch.tensor([0.5], device="cuda")
+    dH1, dW = kd.kd_fused_chunked_kl_bwd(d["H"], d["W"], d["idx"], d["logp"], d["mask"], fw["lse"], g, plan=fw["plan"])
+    dW1 = dW.clone()
+    dH2, dW = kd.kd_fused_chunked_kl_bwd(d["H"], d["W"], d["idx"], d["logp"], d["mask"], fw["lse"], g,
+                                         dW=dW, plan=fw["plan"])
+    torch.cuda.synchronize()
+    assert torch.equal(dH1, dH2)
+    if chunk >= 300:  # one chunk: 0 + a, then a + a, both exact
+        assert torch.equal(dW, dW1 * 2)
+    else:             # several chunks: the second call adds chunk by chunk onto dW1
+        assert rel_fro(dW.cpu().double().numpy(), 2 * dW1.cpu().double().numpy()) <= 1e-6
+    b = O.backward(inp["H"], inp["W"], inp["idx"].numpy(), inp["logp"], inp["mask"].numpy(), grad_loss=0.5)
+    assert rel_fro(dW1.cpu().double().numpy(), b["dW"]) <= 1e-2
+
+
+def test_validation_reports_out_of_range_ids():
+    inp = synth.make_custom(128, 64, 500, 8, "bf16", "ones", "uniform", seed=15)
+    inp["idx"][5, 3] = 500
+    d = {k: v.cuda() for k, v in inp.items() if torch.is_tensor(v)}
+    kd.kd_set_validate(True)
+    try:
+        with pytest.raises(kd.KdError) as e:
+            kd.kd_fused_chunked_kl_fwd(d["H"], d["W"], d["idx"], d["logp"], d["mask"], chunk=64)
+        assert e.value.status == -4
+    finally:
+        kd.kd_set_validate(False)
+    # without validation the id is skipped, nothing is read out of range
+    out = kd.kd_fused_chunked_kl_fwd(d["H"], d["W"], d["idx"], d["logp"], d["mask"], chunk=64)
+    torch.cuda.synchronize()
+    assert np.isfinite(out["loss"].item())
+
+
+def test_autograd_function():
+    inp = synth.make_custom(320, 128, 1100, 10, "bf16", "random5", "uniform", seed=16)
+    d = {k: v.cuda() for k, v in inp.items() if torch.is_tensor(v)}
+    H = d["H"].clone().requires_grad_(True)
+    W = d["W"].clone().requires_grad_(True)
+    loss = kd.fused_chunked_kl(H, W, d["idx"], d["logp"], d["mask"], chunk=128) * 2.0
+    loss.backward()
+    b = O.backward(inp["H"], inp["W"], inp["idx"].numpy(), inp["logp"], inp["mask"].numpy(), grad_loss=2.0)
+    assert rel_fro(H.grad.float().cpu().double().numpy(), b["dH"]) <= 1e-2
+    assert rel_fro(W.grad.float().cpu().double().numpy(), b["dW"]) <= 1e-2
+
+
+# ------------------------------------------------------------------ gather, bit exact
+@pytest.mark.parametrize("T,d,V,K,chunk", [(700, 64, 1000, 20, 256), (32768, 2880, 201088, 100, 0)])
+def test_gather_integer_encoded_exact(T, d, V, K, chunk):
+    # W[v, 0:3] = base-256 digits of v, H[t, 0:3] = (65536, 256, 1): every logit
+    # z_{t,v} = v exactly in bf16 x bf16 -> fp32, so the gathered value must equal the id.
+    inp = synth.make_custom(T, d, V, K, "bf16", "random5", "uniform", seed=17)
+    v = torch.arange(V)
+    W = torch.zeros(V, d)
+    W[:, 0], W[:, 1], W[:, 2] = (v // 65536).float(), ((v // 256) % 256).float(), (v % 256).float()
+    H = torch.zeros(T, d)
+    H[:, 0], H[:, 1], H[:, 2] = 65536.0, 256.0, 1.0
+    inp["W"], inp["H"] = W.to(torch.bfloat16), H.to(torch.bfloat16)
+    gpu = run_gpu(inp, chunk=chunk)
+    live = inp["mask"].numpy() != 0
+    assert np.array_equal(gpu["g"][live], inp["idx"].numpy()[live].astype(np.float64))
+
+
+# ------------------------------------------------------------------ the five workloads
+def test_workload1_tiny_fp32():
+    inp = synth.make_inputs(1)
+    gpu = run_gpu(inp, chunk=64)
+    check_full(inp, gpu, "f32")
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_workload_subset(cfg):
+    inp = synth.make_inputs(cfg)
+    _log(f"  generated inputs for workload {cfg}")
+    res = check_subset(inp, chunk=0, dtype="bf16")
+    _log(f"  workload {cfg}: {res}")
