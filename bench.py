@@ -73,9 +73,21 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--chunk", type=int, default=0)
-    ap.add_argument("--cpu-rows", type=int, default=64, help="rows of the oracle baseline sample")
+    ap.add_argument("--cpu-rows", type=int, default=512, help="rows of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (3 times), to scale HBM byte counters")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1.0)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": src.numel() * 4, "copies": 3}), flush=True)
+        return 0
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the loss head is measured on a single MI355X "
               "(see the sharding notes in DESIGN.md); --gpus must be 1", file=sys.stderr)
