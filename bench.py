@@ -73,7 +73,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--chunk", type=int, default=0)
-    ap.add_argument("--cpu-rows", type=int, default=512, help="rows of the oracle baseline sample")
+    ap.add_argument("--cpu-rows", type=int, default=2048, help="rows of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (3 times), to scale HBM byte counters")

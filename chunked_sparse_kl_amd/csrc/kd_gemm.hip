@@ -46,9 +46,10 @@ struct Traits<float> {
 
 template <int BN>
 struct Smem {
-  static constexpr int kStage = (BM + BN) * ROWB;
-  static constexpr int kBytes = 2 * kStage;
+  static constexpr int kStage = (BM + BN) * ROWB;   // one K block of A and B
 };
+
+#define KD_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
 // LDS staging of epilogue values: 64 token slots x 256 vocab entries (fp32),
 // row pitch padded to keep the 16-byte stores conflict free.
@@ -109,94 +110,165 @@ struct Operand {
 };
 
 // Main loop: accumulates the tile (tm, tn) over K blocks [kb0, kb1).
+//
+// Operands move global -> LDS by direct-to-LDS buffer loads
+// (buffer_load_dwordx4 ... lds): one wavefront instruction writes 8 staged
+// rows (1 KB) at a wave-uniform LDS address, lane L at +16 L.  The XOR swizzle
+// of the 16-byte chunks is applied on the global side: lane L fetches chunk
+// (L%8) ^ (row%8) of its row, so LDS holds chunk c of row r at position
+// c ^ (r%8).  Each tile gets a buffer resource covering exactly its valid rows;
+// lanes of rows past the operand end use an out-of-range offset (the hardware
+// range check skips them; those rows' results are never stored).  A K block
+// that runs past the contraction end is instead loaded through registers with
+// ordinary buffer loads, whose out-of-range chunks read as zero.  The two stage
+// buffers are two distinct LDS arrays so the compiler can see that filling one
+// never aliases reads of the other; each wavefront waits for its own loads and
+// a barrier publishes them to all.
 template <typename T, int BN>
-__device__ inline void gemm_mainloop(const Operand& A, const Operand& B, int k_elems, int tm, int tn,
-                                     int kb0, int kb1, char* smem, f32x16 (&acc)[4][BN / 64]) {
-  constexpr int BK = Traits<T>::BK;
-  constexpr int EPC = 16 / sizeof(T);            // elements per 16-byte chunk
-  constexpr int A_LD = BM * 8 / kThreads;        // 16-byte loads per thread per K block
-  constexpr int B_LD = BN * 8 / kThreads;
-  constexpr int NBJ = BN / 64;
-  constexpr int kStage = Smem<BN>::kStage;
+struct MainLoop {
+  static constexpr int BK = Traits<T>::BK;
+  static constexpr int EPC = 16 / sizeof(T);      // elements per 16-byte chunk
+  static constexpr int A_LD = BM / 32;            // wavefront load instructions per K block (A)
+  static constexpr int B_LD = BN / 32;
+  static constexpr int NBJ = BN / 64;
+  static constexpr unsigned kOut = 0x80000000u;   // beyond any tile's num_records
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wr = wave >> 1, wc = wave & 1;
-  const int r32 = lane & 31, h = lane >> 5;
+  __amdgpu_buffer_rsrc_t ra, rb;
+  unsigned a_off, b_off;     // this lane's byte offset for load i = 0 (row r, chunk c)
+  unsigned a_step, b_step;   // 32 rows, bytes
+  int a_valid, b_valid;      // valid rows of the tile
+  int r;                     // this lane's row within its wavefront's 8
+  int c;                     // logical chunk fetched by this lane
+  int k_elems;
+  int wave_row;              // wave * 8 (uniform)
 
-#pragma unroll
-  for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-    for (int bj = 0; bj < NBJ; ++bj)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[bi][bj][e] = 0.f;
+  __device__ inline void init(const Operand& A, const Operand& B, int ke, int tm, int tn) {
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    wave_row = w * 8;
+    r = lane >> 3;
+    c = (lane & 7) ^ (r & 7);
+    k_elems = ke;
+    a_valid = min(A.rows - tm * BM, BM);
+    b_valid = min(B.rows - tn * BN, BN);
+    const char* a_tile = A.base + (long long)tm * BM * A.ld;
+    const char* b_tile = B.base + (long long)tn * BN * B.ld;
+    ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(a_tile), (short)0,
+                                           (int)(a_valid * A.ld), 0x00020000);
+    rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(b_tile), (short)0,
+                                           (int)(b_valid * B.ld), 0x00020000);
+    a_off = (unsigned)((wave_row + r) * A.ld + c * 16);
+    b_off = (unsigned)((wave_row + r) * B.ld + c * 16);
+    a_step = (unsigned)(32 * A.ld);
+    b_step = (unsigned)(32 * B.ld);
+  }
 
-  // Per-thread load slots: chunk q = i*256 + tid -> row q/8 = i*32 + tid/8 and
-  // 16-byte chunk tid%8, the same chunk for every slot i of a thread.
-  const int row0 = tid >> 3, c = tid & 7;
-  const int kc = c * EPC;
-  const int a_row = tm * BM + row0, b_row = tn * BN + row0;
-  const char* a_src = A.base + (long long)a_row * A.ld + c * 16;
-  const char* b_src = B.base + (long long)b_row * B.ld + c * 16;
-  const long long a_step = 32 * A.ld, b_step = 32 * B.ld;
-  const int dst0 = row0 * ROWB + ((c ^ (row0 & 7)) << 4);  // + i*32*ROWB
-
-  uint4 ra[A_LD], rb[B_LD];
-  auto gload = [&](int kb) {
-    const bool k_ok = kb * BK + kc < k_elems;
-    const long long off = (long long)kb * ROWB;
+  // Issues the direct-to-LDS loads of a full K block kb into stage buffer `st`.
+  __device__ inline void issue(int kb, char* st) const {
+    const unsigned koff = (unsigned)kb * ROWB;
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) {
-      ra[i] = (k_ok && a_row + 32 * i < A.rows)
-                  ? *reinterpret_cast<const uint4*>(a_src + i * a_step + off)
-                  : make_uint4(0, 0, 0, 0);
+      const unsigned off = (wave_row + r + 32 * i < a_valid) ? a_off + i * a_step + koff : kOut;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, KD_LDS(st + (i * 32 + wave_row) * ROWB), 16, off, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
-      rb[i] = (k_ok && b_row + 32 * i < B.rows)
-                  ? *reinterpret_cast<const uint4*>(b_src + i * b_step + off)
-                  : make_uint4(0, 0, 0, 0);
+      const unsigned off = (wave_row + r + 32 * i < b_valid) ? b_off + i * b_step + koff : kOut;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, KD_LDS(st + BM * ROWB + (i * 32 + wave_row) * ROWB), 16,
+                                               off, 0, 0, 0);
     }
-  };
-  auto lstore = [&](int st) {
-    char* base = smem + st * kStage + dst0;
-#pragma unroll
-    for (int i = 0; i < A_LD; ++i) *reinterpret_cast<uint4*>(base + i * 32 * ROWB) = ra[i];
-#pragma unroll
-    for (int i = 0; i < B_LD; ++i)
-      *reinterpret_cast<uint4*>(base + BM * ROWB + i * 32 * ROWB) = rb[i];
-  };
-
-  if (kb0 < kb1) {
-    gload(kb0);
-    lstore(0);
   }
-  __syncthreads();
-  const int a_row0 = (wr * 128 + r32) * ROWB;
-  const int b_row0 = BM * ROWB + (wc * (BN / 2) + r32) * ROWB;
-  for (int kb = kb0; kb < kb1; ++kb) {
-    const int st = (kb - kb0) & 1;
-    const bool more = kb + 1 < kb1;
-    if (more) gload(kb + 1);
-    const char* S = smem + st * kStage;
+
+  // The K block that runs past the contraction end, through registers: chunks
+  // at k >= k_elems read as zero (out-of-range offset of an ordinary load).
+  __device__ inline void load_ragged(int kb, char* st) const {
+    const unsigned koff = (unsigned)kb * ROWB;
+    const bool k_ok = kb * BK + c * EPC < k_elems;
+    const int lane_pos = (threadIdx.x & 63) * 16;
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i) {
+      const unsigned off = (k_ok && wave_row + r + 32 * i < a_valid) ? a_off + i * a_step + koff : kOut;
+      const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0));
+      *reinterpret_cast<uint4*>(st + (i * 32 + wave_row) * ROWB + lane_pos) = v;
+    }
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) {
+      const unsigned off = (k_ok && wave_row + r + 32 * i < b_valid) ? b_off + i * b_step + koff : kOut;
+      const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0));
+      *reinterpret_cast<uint4*>(st + BM * ROWB + (i * 32 + wave_row) * ROWB + lane_pos) = v;
+    }
+  }
+
+  // Multiplies the K block staged in `st` into acc, fragments double buffered
+  // across the four 16-element (bf16) / 8-element (fp32) substeps.
+  __device__ inline static void compute(const char* st, f32x16 (&acc)[4][NBJ]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wr = wave >> 1, wc = wave & 1;
+    const int r32 = lane & 31, h = lane >> 5;
+    const char* a_row0 = st + (wr * 128 + r32) * ROWB;
+    const char* b_row0 = st + BM * ROWB + (wc * (BN / 2) + r32) * ROWB;
+    uint4 fa[2][4], fb[2][NBJ];
+    auto load = [&](int s, uint4 (&xa)[4], uint4 (&xb)[NBJ]) {
+      const int ch = ((2 * s + h) ^ (r32 & 7)) << 4;
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi) xa[bi] = *reinterpret_cast<const uint4*>(a_row0 + bi * 32 * ROWB + ch);
+#pragma unroll
+      for (int bj = 0; bj < NBJ; ++bj) xb[bj] = *reinterpret_cast<const uint4*>(b_row0 + bj * 32 * ROWB + ch);
+    };
+    load(0, fa[0], fb[0]);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int ch = ((2 * s + h) ^ (r32 & 7)) << 4;
-      uint4 fa[4], fb[NBJ];
-#pragma unroll
-      for (int bi = 0; bi < 4; ++bi)
-        fa[bi] = *reinterpret_cast<const uint4*>(S + a_row0 + bi * 32 * ROWB + ch);
-#pragma unroll
-      for (int bj = 0; bj < NBJ; ++bj)
-        fb[bj] = *reinterpret_cast<const uint4*>(S + b_row0 + bj * 32 * ROWB + ch);
+      if (s < 3) load(s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-        for (int bj = 0; bj < NBJ; ++bj) mma_block<T>(fa[bi], fb[bj], acc[bi][bj]);
+        for (int bj = 0; bj < NBJ; ++bj) mma_block<T>(fa[s & 1][bi], fb[s & 1][bj], acc[bi][bj]);
     }
-    if (more) lstore(st ^ 1);
-    __syncthreads();
   }
+};
+
+__device__ inline void wait_own_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */ }
+
+template <typename T, int BN>
+__device__ inline void gemm_mainloop(const Operand& A, const Operand& B, int k_elems, int tm, int tn,
+                                     int kb0, int kb1, char* s0, char* s1,
+                                     f32x16 (&acc)[4][BN / 64]) {
+  using ML = MainLoop<T, BN>;
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < ML::NBJ; ++bj)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[bi][bj][e] = 0.f;
+  ML ml;
+  ml.init(A, B, k_elems, tm, tn);
+  const int kb_full = min(kb1, k_elems / ML::BK);  // blocks entirely inside the contraction
+  if (kb0 < kb_full) ml.issue(kb0, s0);
+  int kb = kb0;
+  for (; kb + 1 < kb_full; kb += 2) {
+    wait_own_loads();
+    __syncthreads();
+    ml.issue(kb + 1, s1);
+    __builtin_amdgcn_sched_barrier(0);
+    ML::compute(s0, acc);
+    wait_own_loads();
+    __syncthreads();
+    if (kb + 2 < kb_full) ml.issue(kb + 2, s0);
+    __builtin_amdgcn_sched_barrier(0);
+    ML::compute(s1, acc);
+  }
+  if (kb < kb_full) {
+    wait_own_loads();
+    __syncthreads();
+    ML::compute(s0, acc);
+  }
+  if (kb_full < kb1) {  // ragged last block (at most one)
+    __syncthreads();
+    ml.load_ragged(kb_full, s1);
+    __syncthreads();
+    ML::compute(s1, acc);
+  }
+  __syncthreads();  // every wavefront is done reading the stage buffers
 }
 
 // ------------------------------------------------------------------ forward
@@ -208,11 +280,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Operand A, Operan
                                                                 int tiles_m, int tiles_n,
                                                                 FwdEpilogue ep) {
   constexpr int BN = 256, NBJ = BN / 64;
-  __shared__ __attribute__((aligned(16))) char smem[Smem<BN>::kBytes];
+  __shared__ __attribute__((aligned(16))) char s0[Smem<BN>::kStage];
+  __shared__ __attribute__((aligned(16))) char s1[Smem<BN>::kStage];
   const TileIdx ti = map_tile<4>(tiles_m, tiles_n, 1);
   f32x16 acc[4][NBJ];
   const int kb_end = (k_elems + Traits<T>::BK - 1) / Traits<T>::BK;
-  gemm_mainloop<T, BN>(A, B, k_elems, ti.tm, ti.tn, 0, kb_end, smem, acc);
+  gemm_mainloop<T, BN>(A, B, k_elems, ti.tm, ti.tn, 0, kb_end, s0, s1, acc);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1, r32 = lane & 31, h = lane >> 5;
@@ -249,7 +322,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Operand A, Operan
     tsum[bj] = sm;
   }
   // --- merge the two vocabulary halves (wr = 0, 1) through LDS
-  float2* red = reinterpret_cast<float2*>(smem);
+  float2* red = reinterpret_cast<float2*>(s0);
   if (h == 0) {
 #pragma unroll
     for (int bj = 0; bj < NBJ; ++bj)
@@ -275,7 +348,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Operand A, Operan
   const int h_lo = ep.hit_off[key0 + row_lo / ROW_BLOCK];
   const int h_hi = ep.hit_off[key0 + (row_hi + ROW_BLOCK - 1) / ROW_BLOCK];
   if (h_lo >= h_hi) return;  // uniform over the workgroup
-  float* stg = reinterpret_cast<float*>(smem);
+  // staged slice of a round: 32 tokens x 256 vocab per wavefront column, column
+  // wc = 0 in s0 and wc = 1 in s1
+  float* const stg0 = reinterpret_cast<float*>(s0);
+  float* const stg1 = reinterpret_cast<float*>(s1);
+  float* const my_stg = wc ? stg1 : stg0;
 #pragma unroll
   for (int round = 0; round < NBJ; ++round) {
     __syncthreads();
@@ -285,8 +362,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Operand A, Operan
       for (int i = 0; i < 4; ++i) {
         f32x4 v4 = {acc[bi][round][4 * i + 0], acc[bi][round][4 * i + 1],
                     acc[bi][round][4 * i + 2], acc[bi][round][4 * i + 3]};
-        *reinterpret_cast<f32x4*>(stg + (wc * 32 + r32) * kStgLd + wr * 128 + bi * 32 + 8 * i +
-                                  4 * h) = v4;
+        *reinterpret_cast<f32x4*>(my_stg + r32 * kStgLd + wr * 128 + bi * 32 + 8 * i + 4 * h) = v4;
       }
     __syncthreads();
     for (int x = h_lo + tid; x < h_hi; x += kThreads) {
@@ -295,7 +371,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Operand A, Operan
       if (nl < 0 || nl >= BN || ((nl >> 5) & 3) != round) continue;
       const long long gi = (long long)hk.x * ep.K + hk.y;
       const int vl = ep.idx[gi] - ti.tm * BM;
-      ep.g[gi] = stg[((nl >> 7) * 32 + (nl & 31)) * kStgLd + vl];
+      ep.g[gi] = ((nl >> 7) ? stg1 : stg0)[(nl & 31) * kStgLd + vl];
     }
   }
 }
@@ -311,11 +387,12 @@ __global__ __launch_bounds__(kThreads, 1) void recompute_gemm_kernel(Operand A, 
                                                                       int tiles_n,
                                                                       RecomputeEpilogue ep) {
   constexpr int BN = 256, NBJ = BN / 64;
-  __shared__ __attribute__((aligned(16))) char smem[Smem<BN>::kBytes];
+  __shared__ __attribute__((aligned(16))) char s0[Smem<BN>::kStage];
+  __shared__ __attribute__((aligned(16))) char s1[Smem<BN>::kStage];
   const TileIdx ti = map_tile<4>(tiles_m, tiles_n, 1);
   f32x16 acc[4][NBJ];
   const int kb_end = (k_elems + Traits<T>::BK - 1) / Traits<T>::BK;
-  gemm_mainloop<T, BN>(A, B, k_elems, ti.tm, ti.tn, 0, kb_end, smem, acc);
+  gemm_mainloop<T, BN>(A, B, k_elems, ti.tm, ti.tn, 0, kb_end, s0, s1, acc);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1, r32 = lane & 31, h = lane >> 5;
@@ -346,7 +423,9 @@ __global__ __launch_bounds__(kThreads, 1) void recompute_gemm_kernel(Operand A, 
   const int key0 = ti.tm * ep.n_rb;
   const int h_lo = row_lo < row_hi ? ep.hit_off[key0 + row_lo / ROW_BLOCK] : 0;
   const int h_hi = row_lo < row_hi ? ep.hit_off[key0 + (row_hi + ROW_BLOCK - 1) / ROW_BLOCK] : 0;
-  float* stg = reinterpret_cast<float*>(smem);
+  float* const stg0 = reinterpret_cast<float*>(s0);
+  float* const stg1 = reinterpret_cast<float*>(s1);
+  float* const my_stg = wc ? stg1 : stg0;
   T* G = static_cast<T*>(ep.G);
   T* GT = static_cast<T*>(ep.GT);
   constexpr int EPC = 16 / sizeof(T);
@@ -360,8 +439,7 @@ __global__ __launch_bounds__(kThreads, 1) void recompute_gemm_kernel(Operand A, 
       for (int i = 0; i < 4; ++i) {
         f32x4 v4 = {acc[bi][round][4 * i + 0], acc[bi][round][4 * i + 1],
                     acc[bi][round][4 * i + 2], acc[bi][round][4 * i + 3]};
-        *reinterpret_cast<f32x4*>(stg + (wc * 32 + r32) * kStgLd + wr * 128 + bi * 32 + 8 * i +
-                                  4 * h) = v4;
+        *reinterpret_cast<f32x4*>(my_stg + r32 * kStgLd + wr * 128 + bi * 32 + 8 * i + 4 * h) = v4;
       }
     __syncthreads();
     for (int x = h_lo + tid; x < h_hi; x += kThreads) {
@@ -370,7 +448,7 @@ __global__ __launch_bounds__(kThreads, 1) void recompute_gemm_kernel(Operand A, 
       if (nl < 0 || nl >= BN || ((nl >> 5) & 3) != round) continue;
       const long long gi = (long long)hk.x * ep.K + hk.y;
       const int vl = ep.idx[gi] - ti.tm * BM;
-      atomicAdd(&stg[((nl >> 7) * 32 + (nl & 31)) * kStgLd + vl], -gw * ep.p[gi]);
+      atomicAdd(&((nl >> 7) ? stg1 : stg0)[(nl & 31) * kStgLd + vl], -gw * ep.p[gi]);
     }
     __syncthreads();
     // G rows: 64 token slots x 256 vocab, EPC elements per 16-byte store.
@@ -382,7 +460,7 @@ __global__ __launch_bounds__(kThreads, 1) void recompute_gemm_kernel(Operand A, 
       const int n = ti.tn * BN + (slot >> 5) * 128 + round * 32 + (slot & 31);
       const int v0 = ti.tm * BM + c * EPC;
       if (n < ep.c_pad && v0 < ep.v_pad) {
-        const float* src = stg + slot * kStgLd + c * EPC;
+        const float* src = ((slot >> 5) ? stg1 : stg0) + (slot & 31) * kStgLd + c * EPC;
         T tmp[EPC];
 #pragma unroll
         for (int u = 0; u < EPC; ++u) tmp[u] = (T)src[u];
@@ -403,7 +481,7 @@ __global__ __launch_bounds__(kThreads, 1) void recompute_gemm_kernel(Operand A, 
       if (v < ep.v_pad && n0 < ep.c_pad) {
         T tmp[EPC];
 #pragma unroll
-        for (int u = 0; u < EPC; ++u) tmp[u] = (T)stg[(seg * 32 + cq * EPC + u) * kStgLd + vl];
+        for (int u = 0; u < EPC; ++u) tmp[u] = (T)(seg ? stg1 : stg0)[(cq * EPC + u) * kStgLd + vl];
         *reinterpret_cast<uint4*>(GT + (long long)v * ep.c_pad + n0) =
             *reinterpret_cast<const uint4*>(tmp);
       }
@@ -421,32 +499,44 @@ __global__ __launch_bounds__(kThreads, 1) void plain_gemm_kernel(Operand A, Oper
                                                                   long long split_stride, int M,
                                                                   int N) {
   constexpr int BN = TILE_D, NBJ = BN / 64;
-  __shared__ __attribute__((aligned(16))) char smem[Smem<BN>::kBytes];
+  __shared__ __attribute__((aligned(16))) char s0[Smem<BN>::kStage];
+  __shared__ __attribute__((aligned(16))) char s1[Smem<BN>::kStage];
   const TileIdx ti = map_tile<8>(tiles_m, tiles_n, splits);
   const int kb_total = (k_elems + Traits<T>::BK - 1) / Traits<T>::BK;
   const int kb0 = ti.split * kb_per_split;
   const int kb1 = min(kb0 + kb_per_split, kb_total);
   f32x16 acc[4][NBJ];
-  gemm_mainloop<T, BN>(A, B, k_elems, ti.tm, ti.tn, kb0, kb1, smem, acc);
+  gemm_mainloop<T, BN>(A, B, k_elems, ti.tm, ti.tn, kb0, kb1, s0, s1, acc);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1, r32 = lane & 31, h = lane >> 5;
   float* o = out + ti.split * split_stride;
+  // One 32x32 block at a time: for accumulation, all 16 old values are loaded
+  // before any store so the loads are issued back to back.
 #pragma unroll
   for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
     for (int bj = 0; bj < NBJ; ++bj) {
       const int n = ti.tn * BN + wc * (BN / 2) + bj * 32 + r32;
-      if (n >= N) continue;
+      const int m0 = ti.tm * BM + wr * 128 + bi * 32 + 4 * h;
+      const bool n_ok = n < N;
+      if (kAccumulate) {
+        float old[16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int m = ti.tm * BM + wr * 128 + bi * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-        if (m < M) {
-          float* dst = o + (long long)m * ld_out + n;
-          if (kAccumulate)
-            *dst += acc[bi][bj][e];
-          else
-            *dst = acc[bi][bj][e];
+        for (int e = 0; e < 16; ++e) {
+          const int m = m0 + 8 * (e >> 2) + (e & 3);
+          old[e] = (n_ok && m < M) ? __builtin_nontemporal_load(o + (long long)m * ld_out + n) : 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int m = m0 + 8 * (e >> 2) + (e & 3);
+          if (n_ok && m < M) o[(long long)m * ld_out + n] = old[e] + acc[bi][bj][e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int m = m0 + 8 * (e >> 2) + (e & 3);
+          if (n_ok && m < M) o[(long long)m * ld_out + n] = acc[bi][bj][e];
         }
       }
     }
