@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <cmath>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -136,15 +137,29 @@ struct Layout {
   size_t G, GT, WT, HT, dhpart, bwd_end;
 };
 
+// Split-K factor of dH = G W (K = V is long, the output C x d is small): the
+// smallest factor >= 4 whose grid is a whole number of waves over the 256 CUs
+// of an MI355X, else the factor in [4, 16] with the least idle tail; never
+// fewer than 16 K blocks per split.
+constexpr int kComputeUnits = 256;
+
 int dh_splits(DType dt, int64_t c_pad, int64_t d, int64_t v_pad) {
   const int64_t tiles = ((c_pad + 255) / 256) * ((d + kd::TILE_D - 1) / kd::TILE_D);
-  const int64_t bk = dt == DType::BF16 ? 64 : 32;
+  const int64_t bk = dt == DType::BF16 ? 32 : 16;
   const int64_t kb_total = (v_pad + bk - 1) / bk;
-  int64_t s = (1024 + tiles - 1) / tiles;
-  s = std::min<int64_t>(s, 32);
-  s = std::min<int64_t>(s, std::max<int64_t>(1, kb_total / 16));
-  s = std::max<int64_t>(s, 1);
-  const int64_t kb_per = (kb_total + s - 1) / s;
+  const int64_t s_max = std::max<int64_t>(1, std::min<int64_t>(16, kb_total / 16));
+  int64_t best = 1;
+  double best_eff = -1.0;
+  for (int64_t s = std::min<int64_t>(4, s_max); s <= s_max; ++s) {
+    const double waves = double(tiles * s) / kComputeUnits;
+    const double eff = waves / std::ceil(waves);
+    if (eff > best_eff + 1e-9) {
+      best_eff = eff;
+      best = s;
+    }
+    if (eff > 0.999) break;
+  }
+  const int64_t kb_per = (kb_total + best - 1) / best;
   return (int)((kb_total + kb_per - 1) / kb_per);
 }
 

@@ -8,10 +8,9 @@
 // A 256-thread workgroup (4 wavefronts in a 2x2 grid) owns a 256 x BN tile;
 // each wavefront owns 128 x BN/2 and accumulates it in 32x32 MFMA blocks
 // (v_mfma_f32_32x32x16_bf16 for bf16, v_mfma_f32_32x32x2f32 for fp32).  The
-// K loop stages 128-byte rows of A and B through LDS, double buffered, with an
-// XOR swizzle of the 16-byte chunks so that both the row-wise stores and the
-// fragment loads are free of bank conflicts; the next K block is fetched into
-// registers while the current one is multiplied.
+// K loop stages 64-byte rows of A and B (one K block) through LDS with
+// direct-to-LDS loads, four stages deep, so three K blocks are in flight while
+// one is multiplied.
 //
 // Accumulator layout of one 32x32 block (lane l, register e = 4*i + j):
 //   row  = 8*i + 4*(l / 32) + j,   column = l % 32.
@@ -30,30 +29,72 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
 
 constexpr int BM = 256;
-constexpr int ROWB = 128;         // bytes per staged row of A or B (one K block)
+constexpr int ROWB = 64;          // bytes per staged row of A or B (one K block)
 constexpr int kThreads = 256;
+constexpr int kStages = 4;        // LDS stage buffers of the K loop
 
 template <typename T>
 struct Traits;
 template <>
 struct Traits<__bf16> {
-  static constexpr int BK = 64;   // K elements per block (128 bytes)
+  static constexpr int BK = 32;   // K elements per block (64 bytes)
 };
 template <>
 struct Traits<float> {
-  static constexpr int BK = 32;
+  static constexpr int BK = 16;
 };
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource of a raw (stride 0) buffer of num_records bytes at base.
+__device__ inline i32x4 make_rsrc(const void* base, unsigned num_records) {
+  const unsigned long long a = reinterpret_cast<unsigned long long>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((unsigned)(a >> 32) & 0xFFFFu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)num_records);
+  r[3] = 0x00020000;
+  return r;
+}
+
+__device__ inline unsigned lds_addr(const void* p) {
+  return (unsigned)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p);
+}
+
+// 16 bytes per lane from buffer offset voff into LDS at lds + 16 * lane.  The
+// instruction has no register destination; m0, voff and the resource are read
+// at issue.  The compiler does not see the LDS write, so the caller orders it
+// with explicit vmcnt waits and barriers (only these loads are in flight in
+// the K loop).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ inline void dma16(i32x4 rsrc, unsigned voff, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(lds)
+               : "m0");
+}
+#pragma clang diagnostic pop
+
+// LDS staging of epilogue values: 64 token slots x 256 vocab entries (fp32),
+// row pitch padded to keep the 16-byte stores conflict free; the 32 slots of
+// one wavefront column live in one stage array.
+constexpr int kStgLd = BM + 4;
+constexpr int kStgBytes = 32 * kStgLd * 4;
 
 template <int BN>
 struct Smem {
   static constexpr int kStage = (BM + BN) * ROWB;   // one K block of A and B
+  static constexpr int kArray = kStage > kStgBytes ? kStage : kStgBytes;
 };
 
-#define KD_LDS(p) ((__attribute__((address_space(3))) void*)(p))
-
-// LDS staging of epilogue values: 64 token slots x 256 vocab entries (fp32),
-// row pitch padded to keep the 16-byte stores conflict free.
-constexpr int kStgLd = BM + 4;
+// The stage buffers are distinct LDS arrays so the compiler can see that
+// filling one never aliases reads of another.
+#define KD_DECLARE_STAGES(BN)                                                   \
+  __shared__ __attribute__((aligned(16))) char st0[Smem<BN>::kArray];          \
+  __shared__ __attribute__((aligned(16))) char st1[Smem<BN>::kArray];          \
+  __shared__ __attribute__((aligned(16))) char st2[Smem<BN>::kArray];          \
+  __shared__ __attribute__((aligned(16))) char st3[Smem<BN>::kArray]
 
 struct TileIdx {
   int tm, tn, split;
@@ -112,70 +153,91 @@ struct Operand {
 // Main loop: accumulates the tile (tm, tn) over K blocks [kb0, kb1).
 //
 // Operands move global -> LDS by direct-to-LDS buffer loads
-// (buffer_load_dwordx4 ... lds): one wavefront instruction writes 8 staged
-// rows (1 KB) at a wave-uniform LDS address, lane L at +16 L.  The XOR swizzle
-// of the 16-byte chunks is applied on the global side: lane L fetches chunk
-// (L%8) ^ (row%8) of its row, so LDS holds chunk c of row r at position
-// c ^ (r%8).  Each tile gets a buffer resource covering exactly its valid rows;
-// lanes of rows past the operand end use an out-of-range offset (the hardware
-// range check skips them; those rows' results are never stored).  A K block
-// that runs past the contraction end is instead loaded through registers with
-// ordinary buffer loads, whose out-of-range chunks read as zero.  The two stage
-// buffers are two distinct LDS arrays so the compiler can see that filling one
-// never aliases reads of the other; each wavefront waits for its own loads and
-// a barrier publishes them to all.
+// (buffer_load_dwordx4 ... lds): one wavefront instruction writes 16 staged
+// rows of 64 bytes (1 KB) at a wave-uniform LDS address, lane L at +16 L.  The
+// XOR swizzle of the 16-byte chunks is applied on the global side: lane L
+// fetches chunk (L%4) ^ ((row/4)%4) of its row, so LDS holds chunk c of row r
+// at position c ^ ((r/4)%4) and a fragment read by 16 consecutive rows touches
+// 16 distinct 16-byte bank groups (64 banks).  Each tile gets a buffer resource
+// covering exactly its valid rows; lanes of rows past the operand end use an
+// out-of-range offset (skipped by the hardware range check; those rows'
+// results are never stored).  The one K block that runs past the contraction
+// end is loaded through registers with ordinary buffer loads, whose
+// out-of-range chunks read as zero.  K block kb+3 is issued while kb is
+// multiplied; each wavefront waits for its own loads of kb (vmcnt) and a
+// barrier publishes them to all.
 template <typename T, int BN>
 struct MainLoop {
   static constexpr int BK = Traits<T>::BK;
   static constexpr int EPC = 16 / sizeof(T);      // elements per 16-byte chunk
-  static constexpr int A_LD = BM / 32;            // wavefront load instructions per K block (A)
-  static constexpr int B_LD = BN / 32;
+  static constexpr int A_LD = BM / 64;            // per-wavefront load instructions per K block (A)
+  static constexpr int B_LD = BN / 64;
+  static constexpr int LOADS = A_LD + B_LD;
   static constexpr int NBJ = BN / 64;
   static constexpr unsigned kOut = 0x80000000u;   // beyond any tile's num_records
 
-  __amdgpu_buffer_rsrc_t ra, rb;
+  i32x4 ra, rb;
+  const char* a_tile;        // first row of the tile (for the ragged block's ordinary loads)
+  const char* b_tile;
+  unsigned a_bytes, b_bytes; // bytes of the tile's valid rows
   unsigned a_off, b_off;     // this lane's byte offset for load i = 0 (row r, chunk c)
-  unsigned a_step, b_step;   // 32 rows, bytes
+  unsigned a_step, b_step;   // 64 rows, bytes
   int a_valid, b_valid;      // valid rows of the tile
-  int r;                     // this lane's row within its wavefront's 8
+  int r;                     // this lane's row within its wavefront's 16
   int c;                     // logical chunk fetched by this lane
   int k_elems;
-  int wave_row;              // wave * 8 (uniform)
+  int wave_row;              // wave * 16 (uniform)
 
   __device__ inline void init(const Operand& A, const Operand& B, int ke, int tm, int tn) {
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    wave_row = w * 8;
-    r = lane >> 3;
-    c = (lane & 7) ^ (r & 7);
+    wave_row = w * 16;
+    r = lane >> 2;
+    c = (lane & 3) ^ ((r >> 2) & 3);
     k_elems = ke;
     a_valid = min(A.rows - tm * BM, BM);
     b_valid = min(B.rows - tn * BN, BN);
-    const char* a_tile = A.base + (long long)tm * BM * A.ld;
-    const char* b_tile = B.base + (long long)tn * BN * B.ld;
-    ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(a_tile), (short)0,
-                                           (int)(a_valid * A.ld), 0x00020000);
-    rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(b_tile), (short)0,
-                                           (int)(b_valid * B.ld), 0x00020000);
+    a_tile = A.base + (long long)tm * BM * A.ld;
+    b_tile = B.base + (long long)tn * BN * B.ld;
+    a_bytes = (unsigned)(a_valid * A.ld);
+    b_bytes = (unsigned)(b_valid * B.ld);
+    ra = make_rsrc(a_tile, a_bytes);
+    rb = make_rsrc(b_tile, b_bytes);
     a_off = (unsigned)((wave_row + r) * A.ld + c * 16);
     b_off = (unsigned)((wave_row + r) * B.ld + c * 16);
-    a_step = (unsigned)(32 * A.ld);
-    b_step = (unsigned)(32 * B.ld);
+    a_step = (unsigned)(64 * A.ld);
+    b_step = (unsigned)(64 * B.ld);
   }
 
   // Issues the direct-to-LDS loads of a full K block kb into stage buffer `st`.
-  __device__ inline void issue(int kb, char* st) const {
+  // With valid == false every lane is out of range: the instructions still
+  // count in vmcnt (so every step waits for the same count) but read nothing.
+  __device__ inline void issue(int kb, char* st, bool valid) const {
     const unsigned koff = (unsigned)kb * ROWB;
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) {
-      const unsigned off = (wave_row + r + 32 * i < a_valid) ? a_off + i * a_step + koff : kOut;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, KD_LDS(st + (i * 32 + wave_row) * ROWB), 16, off, 0, 0, 0);
+      const unsigned off = (valid && wave_row + r + 64 * i < a_valid) ? a_off + i * a_step + koff : kOut;
+      dma16(ra, off, __builtin_amdgcn_readfirstlane(lds_addr(st + (i * 64 + wave_row) * ROWB)));
     }
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
-      const unsigned off = (wave_row + r + 32 * i < b_valid) ? b_off + i * b_step + koff : kOut;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, KD_LDS(st + BM * ROWB + (i * 32 + wave_row) * ROWB), 16,
-                                               off, 0, 0, 0);
+      const unsigned off = (valid && wave_row + r + 64 * i < b_valid) ? b_off + i * b_step + koff : kOut;
+      dma16(rb, off, __builtin_amdgcn_readfirstlane(lds_addr(st + BM * ROWB + (i * 64 + wave_row) * ROWB)));
+    }
+  }
+
+  // Load instruction j (0 <= j < LOADS) of K block kb into stage `st`: j < A_LD
+  // are A rows, the rest B rows; same addressing as issue().
+  __device__ inline void issue_one(int kb, char* st, bool valid, int j) const {
+    const unsigned koff = (unsigned)kb * ROWB;
+    if (j < A_LD) {
+      const int i = j;
+      const unsigned off = (valid && wave_row + r + 64 * i < a_valid) ? a_off + i * a_step + koff : kOut;
+      dma16(ra, off, __builtin_amdgcn_readfirstlane(lds_addr(st + (i * 64 + wave_row) * ROWB)));
+    } else {
+      const int i = j - A_LD;
+      const unsigned off = (valid && wave_row + r + 64 * i < b_valid) ? b_off + i * b_step + koff : kOut;
+      dma16(rb, off, __builtin_amdgcn_readfirstlane(lds_addr(st + BM * ROWB + (i * 64 + wave_row) * ROWB)));
     }
   }
 
@@ -185,53 +247,117 @@ struct MainLoop {
     const unsigned koff = (unsigned)kb * ROWB;
     const bool k_ok = kb * BK + c * EPC < k_elems;
     const int lane_pos = (threadIdx.x & 63) * 16;
+    const __amdgpu_buffer_rsrc_t ba =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(a_tile), (short)0, (int)a_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t bb =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(b_tile), (short)0, (int)b_bytes, 0x00020000);
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) {
-      const unsigned off = (k_ok && wave_row + r + 32 * i < a_valid) ? a_off + i * a_step + koff : kOut;
-      const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0));
-      *reinterpret_cast<uint4*>(st + (i * 32 + wave_row) * ROWB + lane_pos) = v;
+      const unsigned off = (k_ok && wave_row + r + 64 * i < a_valid) ? a_off + i * a_step + koff : kOut;
+      const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ba, off, 0, 0));
+      *reinterpret_cast<uint4*>(st + (i * 64 + wave_row) * ROWB + lane_pos) = v;
     }
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
-      const unsigned off = (k_ok && wave_row + r + 32 * i < b_valid) ? b_off + i * b_step + koff : kOut;
-      const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0));
-      *reinterpret_cast<uint4*>(st + BM * ROWB + (i * 32 + wave_row) * ROWB + lane_pos) = v;
+      const unsigned off = (k_ok && wave_row + r + 64 * i < b_valid) ? b_off + i * b_step + koff : kOut;
+      const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(bb, off, 0, 0));
+      *reinterpret_cast<uint4*>(st + BM * ROWB + (i * 64 + wave_row) * ROWB + lane_pos) = v;
     }
   }
 
-  // Multiplies the K block staged in `st` into acc, fragments double buffered
-  // across the four 16-element (bf16) / 8-element (fp32) substeps.
-  __device__ inline static void compute(const char* st, f32x16 (&acc)[4][NBJ]) {
+  struct Frags {
+    uint4 a[4], b[NBJ];
+  };
+
+  // Fragment loads of substep s (16 bf16 / 8 fp32 K elements) from stage `st`.
+  __device__ inline static void load(const char* st, int s, Frags& f) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wr = wave >> 1, wc = wave & 1;
     const int r32 = lane & 31, h = lane >> 5;
     const char* a_row0 = st + (wr * 128 + r32) * ROWB;
     const char* b_row0 = st + BM * ROWB + (wc * (BN / 2) + r32) * ROWB;
-    uint4 fa[2][4], fb[2][NBJ];
-    auto load = [&](int s, uint4 (&xa)[4], uint4 (&xb)[NBJ]) {
-      const int ch = ((2 * s + h) ^ (r32 & 7)) << 4;
+    const int ch = ((2 * s + h) ^ ((r32 >> 2) & 3)) << 4;
 #pragma unroll
-      for (int bi = 0; bi < 4; ++bi) xa[bi] = *reinterpret_cast<const uint4*>(a_row0 + bi * 32 * ROWB + ch);
+    for (int bi = 0; bi < 4; ++bi) f.a[bi] = *reinterpret_cast<const uint4*>(a_row0 + bi * 32 * ROWB + ch);
 #pragma unroll
-      for (int bj = 0; bj < NBJ; ++bj) xb[bj] = *reinterpret_cast<const uint4*>(b_row0 + bj * 32 * ROWB + ch);
-    };
-    load(0, fa[0], fb[0]);
+    for (int bj = 0; bj < NBJ; ++bj) f.b[bj] = *reinterpret_cast<const uint4*>(b_row0 + bj * 32 * ROWB + ch);
+  }
+
+  __device__ inline static void mma(const Frags& f, f32x16 (&acc)[4][NBJ]) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      if (s < 3) load(s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+    for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-      for (int bi = 0; bi < 4; ++bi)
+      for (int bj = 0; bj < NBJ; ++bj) mma_block<T>(f.a[bi], f.b[bj], acc[bi][bj]);
+  }
+
+  // Multiplies the K block staged in `cur` whose first-substep fragments are
+  // already in f0.  Interleaved with the MFMAs: `issue_next` (loads of a later
+  // K block) and the second substep's fragments during the first substep, and
+  // the first-substep fragments of the next block (stage `pre`) during the
+  // second, so no LDS latency is exposed after the next barrier.
+  template <class F>
+  __device__ inline static void compute(const char* cur, const char* pre, Frags& f0,
+                                        f32x16 (&acc)[4][NBJ], F&& issue_one) {
+    Frags f1;
+    load(cur, 1, f1);
+    int j = 0;
 #pragma unroll
-        for (int bj = 0; bj < NBJ; ++bj) mma_block<T>(fa[s & 1][bi], fb[s & 1][bj], acc[bi][bj]);
+    for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < NBJ; ++bj) {
+        mma_block<T>(f0.a[bi], f0.b[bj], acc[bi][bj]);
+        if (j < LOADS) issue_one(j);  // one load of a later K block per MFMA
+        ++j;
+      }
+#pragma unroll
+    for (int g = 0; g < 4 + NBJ; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    load(pre, 0, f0);
+    mma(f1, acc);
+#pragma unroll
+    for (int g = 0; g < 4 + NBJ; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 };
 
-__device__ inline void wait_own_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */ }
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+template <typename T, int BN>
+struct KLoop {
+  using ML = MainLoop<T, BN>;
+  ML ml;
+  int kb_full;
+  typename ML::Frags f0;  // first-substep fragments of the block about to be multiplied
+
+  // Multiplies K block kb (stage `cur`, fragments of its first substep in f0),
+  // prefetches the first-substep fragments of block kb+1 (stage `pre`) and
+  // issues block kb+3 into `nxt` (the stage of block kb-1).  Before the
+  // barrier each wavefront waits until only block kb+2's loads may still be in
+  // flight, i.e. its loads of kb+1 have landed; the barrier (without a memory
+  // fence, which would wait for everything) then publishes kb+1 and retires
+  // every wavefront's reads of kb-1.
+  __device__ inline void step(int kb, char* cur, char* pre, char* nxt, f32x16 (&acc)[4][BN / 64]) {
+    wait_vmcnt<ML::LOADS>();
+    __builtin_amdgcn_s_barrier();
+    const bool valid = kb + 3 < kb_full;
+    ML::compute(cur, pre, f0, acc, [&](int j) { ml.issue_one(kb + 3, nxt, valid, j); });
+  }
+};
 
 template <typename T, int BN>
 __device__ inline void gemm_mainloop(const Operand& A, const Operand& B, int k_elems, int tm, int tn,
-                                     int kb0, int kb1, char* s0, char* s1,
+                                     int kb0, int kb1, char* st0, char* st1, char* st2, char* st3,
                                      f32x16 (&acc)[4][BN / 64]) {
   using ML = MainLoop<T, BN>;
 #pragma unroll
@@ -240,35 +366,35 @@ __device__ inline void gemm_mainloop(const Operand& A, const Operand& B, int k_e
     for (int bj = 0; bj < ML::NBJ; ++bj)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[bi][bj][e] = 0.f;
-  ML ml;
-  ml.init(A, B, k_elems, tm, tn);
-  const int kb_full = min(kb1, k_elems / ML::BK);  // blocks entirely inside the contraction
-  if (kb0 < kb_full) ml.issue(kb0, s0);
+  KLoop<T, BN> L;
+  L.ml.init(A, B, k_elems, tm, tn);
+  L.kb_full = min(kb1, k_elems / ML::BK);  // blocks entirely inside the contraction
+  const int kb_full = L.kb_full;
+  L.ml.issue(kb0 + 0, st0, kb0 + 0 < kb_full);
+  L.ml.issue(kb0 + 1, st1, kb0 + 1 < kb_full);
+  L.ml.issue(kb0 + 2, st2, kb0 + 2 < kb_full);
+  wait_vmcnt<2 * ML::LOADS>();  // block kb0 landed
+  __builtin_amdgcn_s_barrier();
+  ML::load(st0, 0, L.f0);
   int kb = kb0;
-  for (; kb + 1 < kb_full; kb += 2) {
-    wait_own_loads();
-    __syncthreads();
-    ml.issue(kb + 1, s1);
-    __builtin_amdgcn_sched_barrier(0);
-    ML::compute(s0, acc);
-    wait_own_loads();
-    __syncthreads();
-    if (kb + 2 < kb_full) ml.issue(kb + 2, s0);
-    __builtin_amdgcn_sched_barrier(0);
-    ML::compute(s1, acc);
+  for (; kb + 4 <= kb_full; kb += 4) {
+    L.step(kb + 0, st0, st1, st3, acc);
+    L.step(kb + 1, st1, st2, st0, acc);
+    L.step(kb + 2, st2, st3, st1, acc);
+    L.step(kb + 3, st3, st0, st2, acc);
   }
-  if (kb < kb_full) {
-    wait_own_loads();
-    __syncthreads();
-    ML::compute(s0, acc);
-  }
+  if (kb + 0 < kb_full) L.step(kb + 0, st0, st1, st3, acc);
+  if (kb + 1 < kb_full) L.step(kb + 1, st1, st2, st0, acc);
+  if (kb + 2 < kb_full) L.step(kb + 2, st2, st3, st1, acc);
+  wait_vmcnt<0>();      // the trailing out-of-range loads, before LDS is reused
+  __syncthreads();
   if (kb_full < kb1) {  // ragged last block (at most one)
+    L.ml.load_ragged(kb_full, st3);
     __syncthreads();
-    ml.load_ragged(kb_full, s1);
+    ML::load(st3, 0, L.f0);
+    ML::compute(st3, st3, L.f0, acc, [](int) {});
     __syncthreads();
-    ML::compute(s1, acc);
   }
-  __syncthreads();  // every wavefront is done reading the stage buffers
 }
 
 // ------------------------------------------------------------------ forward
@@ -280,12 +406,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Operand A, Operan
                                                                 int tiles_m, int tiles_n,
                                                                 FwdEpilogue ep) {
   constexpr int BN = 256, NBJ = BN / 64;
-  __shared__ __attribute__((aligned(16))) char s0[Smem<BN>::kStage];
-  __shared__ __attribute__((aligned(16))) char s1[Smem<BN>::kStage];
+  KD_DECLARE_STAGES(BN);
   const TileIdx ti = map_tile<4>(tiles_m, tiles_n, 1);
   f32x16 acc[4][NBJ];
   const int kb_end = (k_elems + Traits<T>::BK - 1) / Traits<T>::BK;
-  gemm_mainloop<T, BN>(A, B, k_elems, ti.tm, ti.tn, 0, kb_end, s0, s1, acc);
+  gemm_mainloop<T, BN>(A, B, k_elems, ti.tm, ti.tn, 0, kb_end, st0, st1, st2, st3, acc);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1, r32 = lane & 31, h = lane >> 5;
@@ -322,7 +447,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Operand A, Operan
     tsum[bj] = sm;
   }
   // --- merge the two vocabulary halves (wr = 0, 1) through LDS
-  float2* red = reinterpret_cast<float2*>(s0);
+  float2* red = reinterpret_cast<float2*>(st2);
   if (h == 0) {
 #pragma unroll
     for (int bj = 0; bj < NBJ; ++bj)
@@ -349,9 +474,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Operand A, Operan
   const int h_hi = ep.hit_off[key0 + (row_hi + ROW_BLOCK - 1) / ROW_BLOCK];
   if (h_lo >= h_hi) return;  // uniform over the workgroup
   // staged slice of a round: 32 tokens x 256 vocab per wavefront column, column
-  // wc = 0 in s0 and wc = 1 in s1
-  float* const stg0 = reinterpret_cast<float*>(s0);
-  float* const stg1 = reinterpret_cast<float*>(s1);
+  // wc = 0 in st0 and wc = 1 in st1
+  float* const stg0 = reinterpret_cast<float*>(st0);
+  float* const stg1 = reinterpret_cast<float*>(st1);
   float* const my_stg = wc ? stg1 : stg0;
 #pragma unroll
   for (int round = 0; round < NBJ; ++round) {
@@ -387,12 +512,11 @@ __global__ __launch_bounds__(kThreads, 1) void recompute_gemm_kernel(Operand A, 
                                                                       int tiles_n,
                                                                       RecomputeEpilogue ep) {
   constexpr int BN = 256, NBJ = BN / 64;
-  __shared__ __attribute__((aligned(16))) char s0[Smem<BN>::kStage];
-  __shared__ __attribute__((aligned(16))) char s1[Smem<BN>::kStage];
+  KD_DECLARE_STAGES(BN);
   const TileIdx ti = map_tile<4>(tiles_m, tiles_n, 1);
   f32x16 acc[4][NBJ];
   const int kb_end = (k_elems + Traits<T>::BK - 1) / Traits<T>::BK;
-  gemm_mainloop<T, BN>(A, B, k_elems, ti.tm, ti.tn, 0, kb_end, s0, s1, acc);
+  gemm_mainloop<T, BN>(A, B, k_elems, ti.tm, ti.tn, 0, kb_end, st0, st1, st2, st3, acc);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1, r32 = lane & 31, h = lane >> 5;
@@ -423,8 +547,8 @@ __global__ __launch_bounds__(kThreads, 1) void recompute_gemm_kernel(Operand A, 
   const int key0 = ti.tm * ep.n_rb;
   const int h_lo = row_lo < row_hi ? ep.hit_off[key0 + row_lo / ROW_BLOCK] : 0;
   const int h_hi = row_lo < row_hi ? ep.hit_off[key0 + (row_hi + ROW_BLOCK - 1) / ROW_BLOCK] : 0;
-  float* const stg0 = reinterpret_cast<float*>(s0);
-  float* const stg1 = reinterpret_cast<float*>(s1);
+  float* const stg0 = reinterpret_cast<float*>(st0);
+  float* const stg1 = reinterpret_cast<float*>(st1);
   float* const my_stg = wc ? stg1 : stg0;
   T* G = static_cast<T*>(ep.G);
   T* GT = static_cast<T*>(ep.GT);
@@ -499,14 +623,13 @@ __global__ __launch_bounds__(kThreads, 1) void plain_gemm_kernel(Operand A, Oper
                                                                   long long split_stride, int M,
                                                                   int N) {
   constexpr int BN = TILE_D, NBJ = BN / 64;
-  __shared__ __attribute__((aligned(16))) char s0[Smem<BN>::kStage];
-  __shared__ __attribute__((aligned(16))) char s1[Smem<BN>::kStage];
+  KD_DECLARE_STAGES(BN);
   const TileIdx ti = map_tile<8>(tiles_m, tiles_n, splits);
   const int kb_total = (k_elems + Traits<T>::BK - 1) / Traits<T>::BK;
   const int kb0 = ti.split * kb_per_split;
   const int kb1 = min(kb0 + kb_per_split, kb_total);
   f32x16 acc[4][NBJ];
-  gemm_mainloop<T, BN>(A, B, k_elems, ti.tm, ti.tn, kb0, kb1, s0, s1, acc);
+  gemm_mainloop<T, BN>(A, B, k_elems, ti.tm, ti.tn, kb0, kb1, st0, st1, st2, st3, acc);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1, r32 = lane & 31, h = lane >> 5;

@@ -14,7 +14,7 @@ namespace kd {
 // those buckets must agree on them.
 constexpr int TILE_V = 256;     // vocabulary rows per fused-GEMM tile
 constexpr int TILE_T = 256;     // token columns per fused-GEMM tile
-constexpr int TILE_D = 192;     // hidden-dim columns per dH / dW tile (2880 = 15*192, 3072 = 16*192)
+constexpr int TILE_D = 256;     // hidden-dim columns per dH / dW tile
 constexpr int ROW_BLOCK = 64;   // chunk starts are multiples of this many rows
 constexpr int KPAD = 64;        // contraction lengths of dH / dW are padded to this
 
