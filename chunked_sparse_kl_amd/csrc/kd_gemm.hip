@@ -30,7 +30,6 @@ constexpr float kNegInf = -__builtin_inff();
 
 constexpr int BM = 256;
 constexpr int ROWB = 64;          // bytes per staged row of A or B (one K block)
-constexpr int kThreads = 256;
 constexpr int kStages = 4;        // LDS stage buffers of the K loop
 
 template <typename T>
@@ -166,14 +165,16 @@ struct Operand {
 // out-of-range chunks read as zero.  K block kb+3 is issued while kb is
 // multiplied; each wavefront waits for its own loads of kb (vmcnt) and a
 // barrier publishes them to all.
-template <typename T, int BN>
+template <typename T, int BN, int WC>
 struct MainLoop {
   static constexpr int BK = Traits<T>::BK;
   static constexpr int EPC = 16 / sizeof(T);      // elements per 16-byte chunk
-  static constexpr int A_LD = BM / 64;            // per-wavefront load instructions per K block (A)
-  static constexpr int B_LD = BN / 64;
+  static constexpr int WAVES = 2 * WC;            // 2 wavefront rows x WC columns
+  static constexpr int ROWS_PER_LD = 16 * WAVES;  // staged rows written by one instruction index
+  static constexpr int A_LD = BM / ROWS_PER_LD;   // per-wavefront load instructions per K block (A)
+  static constexpr int B_LD = BN / ROWS_PER_LD;
   static constexpr int LOADS = A_LD + B_LD;
-  static constexpr int NBJ = BN / 64;
+  static constexpr int NBJ = BN / (32 * WC);      // 32-column MFMA blocks per wavefront
   static constexpr unsigned kOut = 0x80000000u;   // beyond any tile's num_records
 
   i32x4 ra, rb;
@@ -181,7 +182,7 @@ struct MainLoop {
   const char* b_tile;
   unsigned a_bytes, b_bytes; // bytes of the tile's valid rows
   unsigned a_off, b_off;     // this lane's byte offset for load i = 0 (row r, chunk c)
-  unsigned a_step, b_step;   // 64 rows, bytes
+  unsigned a_step, b_step;   // ROWS_PER_LD rows, bytes
   int a_valid, b_valid;      // valid rows of the tile
   int r;                     // this lane's row within its wavefront's 16
   int c;                     // logical chunk fetched by this lane
@@ -205,8 +206,8 @@ struct MainLoop {
     rb = make_rsrc(b_tile, b_bytes);
     a_off = (unsigned)((wave_row + r) * A.ld + c * 16);
     b_off = (unsigned)((wave_row + r) * B.ld + c * 16);
-    a_step = (unsigned)(64 * A.ld);
-    b_step = (unsigned)(64 * B.ld);
+    a_step = (unsigned)(ROWS_PER_LD * A.ld);
+    b_step = (unsigned)(ROWS_PER_LD * B.ld);
   }
 
   // Issues the direct-to-LDS loads of a full K block kb into stage buffer `st`.
@@ -216,13 +217,13 @@ struct MainLoop {
     const unsigned koff = (unsigned)kb * ROWB;
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) {
-      const unsigned off = (valid && wave_row + r + 64 * i < a_valid) ? a_off + i * a_step + koff : kOut;
-      dma16(ra, off, __builtin_amdgcn_readfirstlane(lds_addr(st + (i * 64 + wave_row) * ROWB)));
+      const unsigned off = (valid && wave_row + r + ROWS_PER_LD * i < a_valid) ? a_off + i * a_step + koff : kOut;
+      dma16(ra, off, __builtin_amdgcn_readfirstlane(lds_addr(st + (i * ROWS_PER_LD + wave_row) * ROWB)));
     }
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
-      const unsigned off = (valid && wave_row + r + 64 * i < b_valid) ? b_off + i * b_step + koff : kOut;
-      dma16(rb, off, __builtin_amdgcn_readfirstlane(lds_addr(st + BM * ROWB + (i * 64 + wave_row) * ROWB)));
+      const unsigned off = (valid && wave_row + r + ROWS_PER_LD * i < b_valid) ? b_off + i * b_step + koff : kOut;
+      dma16(rb, off, __builtin_amdgcn_readfirstlane(lds_addr(st + BM * ROWB + (i * ROWS_PER_LD + wave_row) * ROWB)));
     }
   }
 
@@ -232,12 +233,12 @@ struct MainLoop {
     const unsigned koff = (unsigned)kb * ROWB;
     if (j < A_LD) {
       const int i = j;
-      const unsigned off = (valid && wave_row + r + 64 * i < a_valid) ? a_off + i * a_step + koff : kOut;
-      dma16(ra, off, __builtin_amdgcn_readfirstlane(lds_addr(st + (i * 64 + wave_row) * ROWB)));
+      const unsigned off = (valid && wave_row + r + ROWS_PER_LD * i < a_valid) ? a_off + i * a_step + koff : kOut;
+      dma16(ra, off, __builtin_amdgcn_readfirstlane(lds_addr(st + (i * ROWS_PER_LD + wave_row) * ROWB)));
     } else {
       const int i = j - A_LD;
-      const unsigned off = (valid && wave_row + r + 64 * i < b_valid) ? b_off + i * b_step + koff : kOut;
-      dma16(rb, off, __builtin_amdgcn_readfirstlane(lds_addr(st + BM * ROWB + (i * 64 + wave_row) * ROWB)));
+      const unsigned off = (valid && wave_row + r + ROWS_PER_LD * i < b_valid) ? b_off + i * b_step + koff : kOut;
+      dma16(rb, off, __builtin_amdgcn_readfirstlane(lds_addr(st + BM * ROWB + (i * ROWS_PER_LD + wave_row) * ROWB)));
     }
   }
 
@@ -253,15 +254,15 @@ struct MainLoop {
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(b_tile), (short)0, (int)b_bytes, 0x00020000);
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) {
-      const unsigned off = (k_ok && wave_row + r + 64 * i < a_valid) ? a_off + i * a_step + koff : kOut;
+      const unsigned off = (k_ok && wave_row + r + ROWS_PER_LD * i < a_valid) ? a_off + i * a_step + koff : kOut;
       const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ba, off, 0, 0));
-      *reinterpret_cast<uint4*>(st + (i * 64 + wave_row) * ROWB + lane_pos) = v;
+      *reinterpret_cast<uint4*>(st + (i * ROWS_PER_LD + wave_row) * ROWB + lane_pos) = v;
     }
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
-      const unsigned off = (k_ok && wave_row + r + 64 * i < b_valid) ? b_off + i * b_step + koff : kOut;
+      const unsigned off = (k_ok && wave_row + r + ROWS_PER_LD * i < b_valid) ? b_off + i * b_step + koff : kOut;
       const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(bb, off, 0, 0));
-      *reinterpret_cast<uint4*>(st + BM * ROWB + (i * 64 + wave_row) * ROWB + lane_pos) = v;
+      *reinterpret_cast<uint4*>(st + BM * ROWB + (i * ROWS_PER_LD + wave_row) * ROWB + lane_pos) = v;
     }
   }
 
@@ -272,10 +273,10 @@ struct MainLoop {
   // Fragment loads of substep s (16 bf16 / 8 fp32 K elements) from stage `st`.
   __device__ inline static void load(const char* st, int s, Frags& f) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wr = wave >> 1, wc = wave & 1;
+    const int wr = wave / WC, wc = wave % WC;
     const int r32 = lane & 31, h = lane >> 5;
     const char* a_row0 = st + (wr * 128 + r32) * ROWB;
-    const char* b_row0 = st + BM * ROWB + (wc * (BN / 2) + r32) * ROWB;
+    const char* b_row0 = st + BM * ROWB + (wc * (BN / WC) + r32) * ROWB;
     const int ch = ((2 * s + h) ^ ((r32 >> 2) & 3)) << 4;
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi) f.a[bi] = *reinterpret_cast<const uint4*>(a_row0 + bi * 32 * ROWB + ch);
@@ -333,9 +334,9 @@ __device__ inline void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
 }
 
-template <typename T, int BN>
+template <typename T, int BN, int WC>
 struct KLoop {
-  using ML = MainLoop<T, BN>;
+  using ML = MainLoop<T, BN, WC>;
   ML ml;
   int kb_full;
   typename ML::Frags f0;  // first-substep fragments of the block about to be multiplied
@@ -347,7 +348,7 @@ struct KLoop {
   // flight, i.e. its loads of kb+1 have landed; the barrier (without a memory
   // fence, which would wait for everything) then publishes kb+1 and retires
   // every wavefront's reads of kb-1.
-  __device__ inline void step(int kb, char* cur, char* pre, char* nxt, f32x16 (&acc)[4][BN / 64]) {
+  __device__ inline void step(int kb, char* cur, char* pre, char* nxt, f32x16 (&acc)[4][ML::NBJ]) {
     wait_vmcnt<ML::LOADS>();
     __builtin_amdgcn_s_barrier();
     const bool valid = kb + 3 < kb_full;
@@ -355,18 +356,18 @@ struct KLoop {
   }
 };
 
-template <typename T, int BN>
+template <typename T, int BN, int WC>
 __device__ inline void gemm_mainloop(const Operand& A, const Operand& B, int k_elems, int tm, int tn,
                                      int kb0, int kb1, char* st0, char* st1, char* st2, char* st3,
-                                     f32x16 (&acc)[4][BN / 64]) {
-  using ML = MainLoop<T, BN>;
+                                     f32x16 (&acc)[4][BN / (32 * WC)]) {
+  using ML = MainLoop<T, BN, WC>;
 #pragma unroll
   for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
     for (int bj = 0; bj < ML::NBJ; ++bj)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[bi][bj][e] = 0.f;
-  KLoop<T, BN> L;
+  KLoop<T, BN, WC> L;
   L.ml.init(A, B, k_elems, tm, tn);
   L.kb_full = min(kb1, k_elems / ML::BK);  // blocks entirely inside the contraction
   const int kb_full = L.kb_full;
@@ -397,23 +398,55 @@ __device__ inline void gemm_mainloop(const Operand& A, const Operand& B, int k_e
   }
 }
 
+// ------------------------------------------------------------------ fused epilogue layout
+// The fused kernels use 2 x kFusedWC wavefronts; wavefront (wr, wc) owns vocab
+// rows [128 wr, +128) and tokens [wc * 256/kFusedWC, +256/kFusedWC) of the tile,
+// i.e. NBJ 32-token MFMA blocks.  Token block tb = wc * NBJ + bj covers tokens
+// [32 tb, +32).  The LDS-staged epilogue works in 4 rounds of 64 contiguous
+// tokens: round r stages token blocks 2r (in st0) and 2r+1 (in st1).
+#ifndef KD_FUSED_WC
+#define KD_FUSED_WC 4
+#endif
+constexpr int kFusedWC = KD_FUSED_WC;
+constexpr int kFusedThreads = 128 * kFusedWC;
+constexpr int kFusedNBJ = 256 / (32 * kFusedWC);
+
+// Stages this wavefront's token blocks of round `round` (fp32) into LDS.
+__device__ inline void stage_round(const f32x16 (&acc)[4][kFusedNBJ], int round, int wr, int wc,
+                                   int r32, int h, float* stg0, float* stg1) {
+#pragma unroll
+  for (int bj = 0; bj < kFusedNBJ; ++bj) {
+    const int tb = wc * kFusedNBJ + bj;
+    if ((tb >> 1) != round) continue;  // uniform per wavefront
+    float* stg = (tb & 1) ? stg1 : stg0;
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f32x4 v4 = {acc[bi][bj][4 * i + 0], acc[bi][bj][4 * i + 1], acc[bi][bj][4 * i + 2],
+                    acc[bi][bj][4 * i + 3]};
+        *reinterpret_cast<f32x4*>(stg + r32 * kStgLd + wr * 128 + bi * 32 + 8 * i + 4 * h) = v4;
+      }
+  }
+}
+
 // ------------------------------------------------------------------ forward
 // D[v][t] = z_{t,v}.  Per token: max and sum of exp(z - max) over this tile's
 // vocabulary rows (-> one (max, sum) partial per vocabulary tile), then the
 // logits at the token's teacher ids are copied out of an LDS-staged slice.
 template <typename T>
-__global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Operand A, Operand B, int k_elems,
-                                                                int tiles_m, int tiles_n,
-                                                                FwdEpilogue ep) {
-  constexpr int BN = 256, NBJ = BN / 64;
+__global__ __launch_bounds__(kFusedThreads, 1) void fwd_gemm_kernel(Operand A, Operand B, int k_elems,
+                                                                     int tiles_m, int tiles_n,
+                                                                     FwdEpilogue ep) {
+  constexpr int BN = 256, NBJ = kFusedNBJ, WC = kFusedWC;
   KD_DECLARE_STAGES(BN);
   const TileIdx ti = map_tile<4>(tiles_m, tiles_n, 1);
   f32x16 acc[4][NBJ];
   const int kb_end = (k_elems + Traits<T>::BK - 1) / Traits<T>::BK;
-  gemm_mainloop<T, BN>(A, B, k_elems, ti.tm, ti.tn, 0, kb_end, st0, st1, st2, st3, acc);
+  gemm_mainloop<T, BN, WC>(A, B, k_elems, ti.tm, ti.tn, 0, kb_end, st0, st1, st2, st3, acc);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wr = wave >> 1, wc = wave & 1, r32 = lane & 31, h = lane >> 5;
+  const int wr = wave / WC, wc = wave % WC, r32 = lane & 31, h = lane >> 5;
   const int v_base = ti.tm * BM + wr * 128 + 4 * h;  // + bi*32 + 8*i + j
   const bool full_v = (ti.tm + 1) * BM <= ep.V;
 
@@ -451,10 +484,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Operand A, Operan
   if (h == 0) {
 #pragma unroll
     for (int bj = 0; bj < NBJ; ++bj)
-      red[wr * BN + wc * 128 + bj * 32 + r32] = make_float2(tmax[bj], tsum[bj]);
+      red[wr * BN + (wc * NBJ + bj) * 32 + r32] = make_float2(tmax[bj], tsum[bj]);
   }
   __syncthreads();
-  {
+  if (tid < BN) {
     const int n = ti.tn * BN + tid;  // one token per thread
     if (n < ep.rows) {
       const float2 a = red[tid], b = red[BN + tid];
@@ -473,30 +506,20 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Operand A, Operan
   const int h_lo = ep.hit_off[key0 + row_lo / ROW_BLOCK];
   const int h_hi = ep.hit_off[key0 + (row_hi + ROW_BLOCK - 1) / ROW_BLOCK];
   if (h_lo >= h_hi) return;  // uniform over the workgroup
-  // staged slice of a round: 32 tokens x 256 vocab per wavefront column, column
-  // wc = 0 in st0 and wc = 1 in st1
   float* const stg0 = reinterpret_cast<float*>(st0);
   float* const stg1 = reinterpret_cast<float*>(st1);
-  float* const my_stg = wc ? stg1 : stg0;
 #pragma unroll
-  for (int round = 0; round < NBJ; ++round) {
+  for (int round = 0; round < 4; ++round) {
     __syncthreads();
-#pragma unroll
-    for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f32x4 v4 = {acc[bi][round][4 * i + 0], acc[bi][round][4 * i + 1],
-                    acc[bi][round][4 * i + 2], acc[bi][round][4 * i + 3]};
-        *reinterpret_cast<f32x4*>(my_stg + r32 * kStgLd + wr * 128 + bi * 32 + 8 * i + 4 * h) = v4;
-      }
+    stage_round(acc, round, wr, wc, r32, h, stg0, stg1);
     __syncthreads();
-    for (int x = h_lo + tid; x < h_hi; x += kThreads) {
+    for (int x = h_lo + tid; x < h_hi; x += kFusedThreads) {
       const int2 hk = ep.hits[x];
-      const int nl = hk.x - row_lo;  // token within the tile
-      if (nl < 0 || nl >= BN || ((nl >> 5) & 3) != round) continue;
+      const int sl = hk.x - row_lo - round * 64;  // staged slot of the token
+      if (sl < 0 || sl >= 64) continue;
       const long long gi = (long long)hk.x * ep.K + hk.y;
       const int vl = ep.idx[gi] - ti.tm * BM;
-      ep.g[gi] = ((nl >> 7) ? stg1 : stg0)[(nl & 31) * kStgLd + vl];
+      ep.g[gi] = ((sl >> 5) ? stg1 : stg0)[(sl & 31) * kStgLd + vl];
     }
   }
 }
@@ -507,19 +530,19 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Operand A, Operan
 // scatter is applied, then rounded to T and written row-major (G) and
 // transposed (G^T).
 template <typename T>
-__global__ __launch_bounds__(kThreads, 1) void recompute_gemm_kernel(Operand A, Operand B,
-                                                                      int k_elems, int tiles_m,
-                                                                      int tiles_n,
-                                                                      RecomputeEpilogue ep) {
-  constexpr int BN = 256, NBJ = BN / 64;
+__global__ __launch_bounds__(kFusedThreads, 1) void recompute_gemm_kernel(Operand A, Operand B,
+                                                                           int k_elems, int tiles_m,
+                                                                           int tiles_n,
+                                                                           RecomputeEpilogue ep) {
+  constexpr int BN = 256, NBJ = kFusedNBJ, WC = kFusedWC;
   KD_DECLARE_STAGES(BN);
   const TileIdx ti = map_tile<4>(tiles_m, tiles_n, 1);
   f32x16 acc[4][NBJ];
   const int kb_end = (k_elems + Traits<T>::BK - 1) / Traits<T>::BK;
-  gemm_mainloop<T, BN>(A, B, k_elems, ti.tm, ti.tn, 0, kb_end, st0, st1, st2, st3, acc);
+  gemm_mainloop<T, BN, WC>(A, B, k_elems, ti.tm, ti.tn, 0, kb_end, st0, st1, st2, st3, acc);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wr = wave >> 1, wc = wave & 1, r32 = lane & 31, h = lane >> 5;
+  const int wr = wave / WC, wc = wave % WC, r32 = lane & 31, h = lane >> 5;
   const int v_base = ti.tm * BM + wr * 128 + 4 * h;
   const bool full_v = (ti.tm + 1) * BM <= ep.V;
   const int nv = ep.ctrl->n_valid;
@@ -527,7 +550,7 @@ __global__ __launch_bounds__(kThreads, 1) void recompute_gemm_kernel(Operand A, 
 
 #pragma unroll
   for (int bj = 0; bj < NBJ; ++bj) {
-    const int n = ti.tn * BN + wc * 128 + bj * 32 + r32;
+    const int n = ti.tn * BN + (wc * NBJ + bj) * 32 + r32;
     const int t = ep.c0 + n;
     const bool live = n < ep.rows && (ep.mask == nullptr || ep.mask[t] != 0);
     const float coef = live ? gw * ep.S[t] : 0.f;
@@ -549,39 +572,32 @@ __global__ __launch_bounds__(kThreads, 1) void recompute_gemm_kernel(Operand A, 
   const int h_hi = row_lo < row_hi ? ep.hit_off[key0 + (row_hi + ROW_BLOCK - 1) / ROW_BLOCK] : 0;
   float* const stg0 = reinterpret_cast<float*>(st0);
   float* const stg1 = reinterpret_cast<float*>(st1);
-  float* const my_stg = wc ? stg1 : stg0;
   T* G = static_cast<T*>(ep.G);
   T* GT = static_cast<T*>(ep.GT);
   constexpr int EPC = 16 / sizeof(T);
 
 #pragma unroll
-  for (int round = 0; round < NBJ; ++round) {
+  for (int round = 0; round < 4; ++round) {
     __syncthreads();
-#pragma unroll
-    for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f32x4 v4 = {acc[bi][round][4 * i + 0], acc[bi][round][4 * i + 1],
-                    acc[bi][round][4 * i + 2], acc[bi][round][4 * i + 3]};
-        *reinterpret_cast<f32x4*>(my_stg + r32 * kStgLd + wr * 128 + bi * 32 + 8 * i + 4 * h) = v4;
-      }
+    stage_round(acc, round, wr, wc, r32, h, stg0, stg1);
     __syncthreads();
-    for (int x = h_lo + tid; x < h_hi; x += kThreads) {
+    for (int x = h_lo + tid; x < h_hi; x += kFusedThreads) {
       const int2 hk = ep.hits[x];
-      const int nl = hk.x - row_lo;
-      if (nl < 0 || nl >= BN || ((nl >> 5) & 3) != round) continue;
+      const int sl = hk.x - row_lo - round * 64;
+      if (sl < 0 || sl >= 64) continue;
       const long long gi = (long long)hk.x * ep.K + hk.y;
       const int vl = ep.idx[gi] - ti.tm * BM;
-      atomicAdd(&((nl >> 7) ? stg1 : stg0)[(nl & 31) * kStgLd + vl], -gw * ep.p[gi]);
+      atomicAdd(&((sl >> 5) ? stg1 : stg0)[(sl & 31) * kStgLd + vl], -gw * ep.p[gi]);
     }
     __syncthreads();
-    // G rows: 64 token slots x 256 vocab, EPC elements per 16-byte store.
+    const int n_round = ti.tn * BN + round * 64;  // first token of the round
+    // G rows: 64 tokens x 256 vocab, EPC elements per 16-byte store.
     constexpr int kRowChunks = BM / EPC;
 #pragma unroll
-    for (int it = 0; it < 64 * kRowChunks / kThreads; ++it) {
-      const int q = it * kThreads + tid;
+    for (int it = 0; it < 64 * kRowChunks / kFusedThreads; ++it) {
+      const int q = it * kFusedThreads + tid;
       const int slot = q / kRowChunks, c = q % kRowChunks;
-      const int n = ti.tn * BN + (slot >> 5) * 128 + round * 32 + (slot & 31);
+      const int n = n_round + slot;
       const int v0 = ti.tm * BM + c * EPC;
       if (n < ep.c_pad && v0 < ep.v_pad) {
         const float* src = ((slot >> 5) ? stg1 : stg0) + (slot & 31) * kStgLd + c * EPC;
@@ -592,20 +608,22 @@ __global__ __launch_bounds__(kThreads, 1) void recompute_gemm_kernel(Operand A, 
             *reinterpret_cast<const uint4*>(tmp);
       }
     }
-    // G^T rows: 256 vocab x (2 segments of 32 tokens), EPC tokens per store.
-    constexpr int kSegChunks = 32 / EPC;
+    // G^T rows: 256 vocab x 64 contiguous tokens, EPC tokens per store.
+    constexpr int kTokChunks = 64 / EPC;
 #pragma unroll
-    for (int it = 0; it < BM * 2 * kSegChunks / kThreads; ++it) {
-      const int q = it * kThreads + tid;
+    for (int it = 0; it < BM * kTokChunks / kFusedThreads; ++it) {
+      const int q = it * kFusedThreads + tid;
       const int vl = q & (BM - 1);
-      const int rest = q / BM;
-      const int seg = rest / kSegChunks, cq = rest % kSegChunks;
+      const int cq = q / BM;
       const int v = ti.tm * BM + vl;
-      const int n0 = ti.tn * BN + seg * 128 + round * 32 + cq * EPC;
+      const int n0 = n_round + cq * EPC;
       if (v < ep.v_pad && n0 < ep.c_pad) {
         T tmp[EPC];
 #pragma unroll
-        for (int u = 0; u < EPC; ++u) tmp[u] = (T)(seg ? stg1 : stg0)[(cq * EPC + u) * kStgLd + vl];
+        for (int u = 0; u < EPC; ++u) {
+          const int sl = cq * EPC + u;
+          tmp[u] = (T)((sl >> 5) ? stg1 : stg0)[(sl & 31) * kStgLd + vl];
+        }
         *reinterpret_cast<uint4*>(GT + (long long)v * ep.c_pad + n0) =
             *reinterpret_cast<const uint4*>(tmp);
       }
@@ -615,24 +633,30 @@ __global__ __launch_bounds__(kThreads, 1) void recompute_gemm_kernel(Operand A, 
 
 // ------------------------------------------------------------------ dH, dW
 // Plain tiles: D[m][n] (n contiguous in the output).  kAccumulate: out += D.
+#ifndef KD_PLAIN_WC
+#define KD_PLAIN_WC 4
+#endif
+constexpr int kPlainWC = KD_PLAIN_WC;          // wavefront columns of the dH / dW tiles
+constexpr int kPlainThreads = 128 * kPlainWC;
+
 template <typename T, bool kAccumulate>
-__global__ __launch_bounds__(kThreads, 1) void plain_gemm_kernel(Operand A, Operand B, int k_elems,
-                                                                  int tiles_m, int tiles_n,
-                                                                  int splits, int kb_per_split,
-                                                                  float* out, long long ld_out,
-                                                                  long long split_stride, int M,
-                                                                  int N) {
-  constexpr int BN = TILE_D, NBJ = BN / 64;
+__global__ __launch_bounds__(kPlainThreads, 1) void plain_gemm_kernel(Operand A, Operand B, int k_elems,
+                                                                       int tiles_m, int tiles_n,
+                                                                       int splits, int kb_per_split,
+                                                                       float* out, long long ld_out,
+                                                                       long long split_stride, int M,
+                                                                       int N) {
+  constexpr int BN = TILE_D, WC = kPlainWC, NBJ = BN / (32 * WC);
   KD_DECLARE_STAGES(BN);
   const TileIdx ti = map_tile<8>(tiles_m, tiles_n, splits);
   const int kb_total = (k_elems + Traits<T>::BK - 1) / Traits<T>::BK;
   const int kb0 = ti.split * kb_per_split;
   const int kb1 = min(kb0 + kb_per_split, kb_total);
   f32x16 acc[4][NBJ];
-  gemm_mainloop<T, BN>(A, B, k_elems, ti.tm, ti.tn, kb0, kb1, st0, st1, st2, st3, acc);
+  gemm_mainloop<T, BN, WC>(A, B, k_elems, ti.tm, ti.tn, kb0, kb1, st0, st1, st2, st3, acc);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wr = wave >> 1, wc = wave & 1, r32 = lane & 31, h = lane >> 5;
+  const int wr = wave / WC, wc = wave % WC, r32 = lane & 31, h = lane >> 5;
   float* o = out + ti.split * split_stride;
   // One 32x32 block at a time: for accumulation, all 16 old values are loaded
   // before any store so the loads are issued back to back.
@@ -640,7 +664,7 @@ __global__ __launch_bounds__(kThreads, 1) void plain_gemm_kernel(Operand A, Oper
   for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
     for (int bj = 0; bj < NBJ; ++bj) {
-      const int n = ti.tn * BN + wc * (BN / 2) + bj * 32 + r32;
+      const int n = ti.tn * BN + wc * (BN / WC) + bj * 32 + r32;
       const int m0 = ti.tm * BM + wr * 128 + bi * 32 + 4 * h;
       const bool n_ok = n < N;
       if (kAccumulate) {
@@ -678,7 +702,7 @@ template <typename T>
 void fwd_impl(const void* W, int V, const void* Hc, int rows, int d, const FwdEpilogue& ep,
               hipStream_t s) {
   const int tiles_m = (V + BM - 1) / BM, tiles_n = (rows + 255) / 256;
-  fwd_gemm_kernel<T><<<tiles_m * tiles_n, kThreads, 0, s>>>(
+  fwd_gemm_kernel<T><<<tiles_m * tiles_n, kFusedThreads, 0, s>>>(
       make_operand<T>(W, d, V), make_operand<T>(Hc, d, rows), d, tiles_m, tiles_n, ep);
 }
 
@@ -686,7 +710,7 @@ template <typename T>
 void recompute_impl(const void* W, int V, const void* Hc, int rows, int d,
                     const RecomputeEpilogue& ep, hipStream_t s) {
   const int tiles_m = (V + BM - 1) / BM, tiles_n = (rows + 255) / 256;
-  recompute_gemm_kernel<T><<<tiles_m * tiles_n, kThreads, 0, s>>>(
+  recompute_gemm_kernel<T><<<tiles_m * tiles_n, kFusedThreads, 0, s>>>(
       make_operand<T>(W, d, V), make_operand<T>(Hc, d, rows), d, tiles_m, tiles_n, ep);
 }
 
@@ -716,11 +740,11 @@ void launch_dh_gemm(DType t, const void* G, int rows, int v_pad, const void* WT,
   const int kb_per = (kb_total + splits - 1) / splits;
   const int grid = tiles_m * tiles_n * splits;
   if (t == DType::BF16)
-    plain_gemm_kernel<__bf16, false><<<grid, kThreads, 0, s>>>(
+    plain_gemm_kernel<__bf16, false><<<grid, kPlainThreads, 0, s>>>(
         make_operand<__bf16>(G, v_pad, rows), make_operand<__bf16>(WT, v_pad, d), v_pad, tiles_m,
         tiles_n, splits, kb_per, part, d, split_stride, rows, d);
   else
-    plain_gemm_kernel<float, false><<<grid, kThreads, 0, s>>>(
+    plain_gemm_kernel<float, false><<<grid, kPlainThreads, 0, s>>>(
         make_operand<float>(G, v_pad, rows), make_operand<float>(WT, v_pad, d), v_pad, tiles_m,
         tiles_n, splits, kb_per, part, d, split_stride, rows, d);
 }
@@ -732,11 +756,11 @@ void launch_dw_gemm(DType t, const void* GT, int V, int c_pad, const void* HT, i
   const int kb_total = (c_pad + bk - 1) / bk;
   const int grid = tiles_m * tiles_n;
   if (t == DType::BF16)
-    plain_gemm_kernel<__bf16, true><<<grid, kThreads, 0, s>>>(
+    plain_gemm_kernel<__bf16, true><<<grid, kPlainThreads, 0, s>>>(
         make_operand<__bf16>(GT, c_pad, V), make_operand<__bf16>(HT, c_pad, d), c_pad, tiles_m,
         tiles_n, 1, kb_total, dW, d, 0, V, d);
   else
-    plain_gemm_kernel<float, true><<<grid, kThreads, 0, s>>>(
+    plain_gemm_kernel<float, true><<<grid, kPlainThreads, 0, s>>>(
         make_operand<float>(GT, c_pad, V), make_operand<float>(HT, c_pad, d), c_pad, tiles_m,
         tiles_n, 1, kb_total, dW, d, 0, V, d);
 }
