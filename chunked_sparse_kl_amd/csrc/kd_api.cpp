@@ -145,7 +145,7 @@ constexpr int kComputeUnits = 256;
 
 int dh_splits(DType dt, int64_t c_pad, int64_t d, int64_t v_pad) {
   const int64_t tiles = ((c_pad + 255) / 256) * ((d + kd::TILE_D - 1) / kd::TILE_D);
-  const int64_t bk = dt == DType::BF16 ? 32 : 16;
+  const int64_t bk = kd::k_block(dt);
   const int64_t kb_total = (v_pad + bk - 1) / bk;
   const int64_t s_max = std::max<int64_t>(1, std::min<int64_t>(16, kb_total / 16));
   int64_t best = 1;

@@ -5,12 +5,12 @@
 //   forward / recompute:  A = W [V][d],      B = H_c [C][d]     (D = logits^T)
 //   dH:                   A = G [C][V],      B = W^T [d][V]     (split over V)
 //   dW:                   A = G^T [V][C],    B = H_c^T [d][C]
-// A 256-thread workgroup (4 wavefronts in a 2x2 grid) owns a 256 x BN tile;
-// each wavefront owns 128 x BN/2 and accumulates it in 32x32 MFMA blocks
-// (v_mfma_f32_32x32x16_bf16 for bf16, v_mfma_f32_32x32x2f32 for fp32).  The
-// K loop stages 64-byte rows of A and B (one K block) through LDS with
-// direct-to-LDS loads, four stages deep, so three K blocks are in flight while
-// one is multiplied.
+// A 512-thread workgroup (8 wavefronts in a 2 x 4 grid, two per SIMD) owns a
+// 256 x 256 tile; each wavefront owns 128 x 64 and accumulates it in 32x32
+// MFMA blocks (v_mfma_f32_32x32x16_bf16 for bf16, v_mfma_f32_32x32x2f32 for
+// fp32).  The K loop stages 128-byte rows of A and B (one K block) through
+// LDS with direct-to-LDS loads into two stages: block kb+1 lands while kb is
+// multiplied, and kb+2 is issued during kb's last substep.
 //
 // Accumulator layout of one 32x32 block (lane l, register e = 4*i + j):
 //   row  = 8*i + 4*(l / 32) + j,   column = l % 32.
@@ -29,19 +29,19 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
 
 constexpr int BM = 256;
-constexpr int ROWB = 64;          // bytes per staged row of A or B (one K block)
-constexpr int kStages = 4;        // LDS stage buffers of the K loop
+constexpr int ROWB = KBLOCK_BYTES;  // bytes per staged row of A or B (one K block)
 
 template <typename T>
 struct Traits;
 template <>
 struct Traits<__bf16> {
-  static constexpr int BK = 32;   // K elements per block (64 bytes)
+  static constexpr int BK = 64;   // K elements per block (128 bytes)
 };
 template <>
 struct Traits<float> {
-  static constexpr int BK = 16;
+  static constexpr int BK = 32;
 };
+static_assert(Traits<__bf16>::BK * 2 == ROWB && Traits<float>::BK * 4 == ROWB, "K block is one staged row");
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
@@ -91,9 +91,7 @@ struct Smem {
 // filling one never aliases reads of another.
 #define KD_DECLARE_STAGES(BN)                                                   \
   __shared__ __attribute__((aligned(16))) char st0[Smem<BN>::kArray];          \
-  __shared__ __attribute__((aligned(16))) char st1[Smem<BN>::kArray];          \
-  __shared__ __attribute__((aligned(16))) char st2[Smem<BN>::kArray];          \
-  __shared__ __attribute__((aligned(16))) char st3[Smem<BN>::kArray]
+  __shared__ __attribute__((aligned(16))) char st1[Smem<BN>::kArray]
 
 struct TileIdx {
   int tm, tn, split;
@@ -152,29 +150,30 @@ struct Operand {
 // Main loop: accumulates the tile (tm, tn) over K blocks [kb0, kb1).
 //
 // Operands move global -> LDS by direct-to-LDS buffer loads
-// (buffer_load_dwordx4 ... lds): one wavefront instruction writes 16 staged
-// rows of 64 bytes (1 KB) at a wave-uniform LDS address, lane L at +16 L.  The
-// XOR swizzle of the 16-byte chunks is applied on the global side: lane L
-// fetches chunk (L%4) ^ ((row/4)%4) of its row, so LDS holds chunk c of row r
-// at position c ^ ((r/4)%4) and a fragment read by 16 consecutive rows touches
-// 16 distinct 16-byte bank groups (64 banks).  Each tile gets a buffer resource
-// covering exactly its valid rows; lanes of rows past the operand end use an
+// (buffer_load_dwordx4 ... lds): one wavefront instruction writes 8 staged
+// rows of 128 bytes (1 KB) at a wave-uniform LDS address, lane L at +16 L, so
+// the 8 lanes of a row fetch one whole 128-byte line (half-line rows double
+// the L1 -> L2 request count, which then limits the loop).  The XOR swizzle of
+// the 16-byte chunks is applied on the global side: lane L fetches chunk
+// (L%8) ^ ((row/2)%8) of its row, so LDS holds chunk c of row r at position
+// c ^ ((r/2)%8) and a fragment read by 16 consecutive rows touches 16 distinct
+// 16-byte bank groups (64 banks).  Each tile gets a buffer resource covering
+// exactly its valid rows; lanes of rows past the operand end use an
 // out-of-range offset (skipped by the hardware range check; those rows'
 // results are never stored).  The one K block that runs past the contraction
 // end is loaded through registers with ordinary buffer loads, whose
-// out-of-range chunks read as zero.  K block kb+3 is issued while kb is
-// multiplied; each wavefront waits for its own loads of kb (vmcnt) and a
-// barrier publishes them to all.
+// out-of-range chunks read as zero.
 template <typename T, int BN, int WC>
 struct MainLoop {
   static constexpr int BK = Traits<T>::BK;
   static constexpr int EPC = 16 / sizeof(T);      // elements per 16-byte chunk
   static constexpr int WAVES = 2 * WC;            // 2 wavefront rows x WC columns
-  static constexpr int ROWS_PER_LD = 16 * WAVES;  // staged rows written by one instruction index
+  static constexpr int ROWS_PER_LD = 8 * WAVES;   // staged rows written by one instruction index
   static constexpr int A_LD = BM / ROWS_PER_LD;   // per-wavefront load instructions per K block (A)
   static constexpr int B_LD = BN / ROWS_PER_LD;
   static constexpr int LOADS = A_LD + B_LD;
   static constexpr int NBJ = BN / (32 * WC);      // 32-column MFMA blocks per wavefront
+  static constexpr int SUB = ROWB / 32;           // MFMA substeps (32 bytes of K) per block
   static constexpr unsigned kOut = 0x80000000u;   // beyond any tile's num_records
 
   i32x4 ra, rb;
@@ -184,17 +183,17 @@ struct MainLoop {
   unsigned a_off, b_off;     // this lane's byte offset for load i = 0 (row r, chunk c)
   unsigned a_step, b_step;   // ROWS_PER_LD rows, bytes
   int a_valid, b_valid;      // valid rows of the tile
-  int r;                     // this lane's row within its wavefront's 16
+  int r;                     // this lane's row within its wavefront's 8
   int c;                     // logical chunk fetched by this lane
   int k_elems;
-  int wave_row;              // wave * 16 (uniform)
+  int wave_row;              // wave * 8 (uniform)
 
   __device__ inline void init(const Operand& A, const Operand& B, int ke, int tm, int tn) {
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    wave_row = w * 16;
-    r = lane >> 2;
-    c = (lane & 3) ^ ((r >> 2) & 3);
+    wave_row = w * 8;
+    r = lane >> 3;
+    c = (lane & 7) ^ (((wave_row + r) >> 1) & 7);
     k_elems = ke;
     a_valid = min(A.rows - tm * BM, BM);
     b_valid = min(B.rows - tn * BN, BN);
@@ -210,25 +209,10 @@ struct MainLoop {
     b_step = (unsigned)(ROWS_PER_LD * B.ld);
   }
 
-  // Issues the direct-to-LDS loads of a full K block kb into stage buffer `st`.
-  // With valid == false every lane is out of range: the instructions still
-  // count in vmcnt (so every step waits for the same count) but read nothing.
-  __device__ inline void issue(int kb, char* st, bool valid) const {
-    const unsigned koff = (unsigned)kb * ROWB;
-#pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-      const unsigned off = (valid && wave_row + r + ROWS_PER_LD * i < a_valid) ? a_off + i * a_step + koff : kOut;
-      dma16(ra, off, __builtin_amdgcn_readfirstlane(lds_addr(st + (i * ROWS_PER_LD + wave_row) * ROWB)));
-    }
-#pragma unroll
-    for (int i = 0; i < B_LD; ++i) {
-      const unsigned off = (valid && wave_row + r + ROWS_PER_LD * i < b_valid) ? b_off + i * b_step + koff : kOut;
-      dma16(rb, off, __builtin_amdgcn_readfirstlane(lds_addr(st + BM * ROWB + (i * ROWS_PER_LD + wave_row) * ROWB)));
-    }
-  }
-
-  // Load instruction j (0 <= j < LOADS) of K block kb into stage `st`: j < A_LD
-  // are A rows, the rest B rows; same addressing as issue().
+  // Load instruction j (0 <= j < LOADS) of the full K block kb into stage
+  // `st`: j < A_LD are A rows, the rest B rows.  With valid == false every
+  // lane is out of range: the instruction still counts in vmcnt (so every
+  // step waits for the same count) but reads nothing.
   __device__ inline void issue_one(int kb, char* st, bool valid, int j) const {
     const unsigned koff = (unsigned)kb * ROWB;
     if (j < A_LD) {
@@ -240,6 +224,11 @@ struct MainLoop {
       const unsigned off = (valid && wave_row + r + ROWS_PER_LD * i < b_valid) ? b_off + i * b_step + koff : kOut;
       dma16(rb, off, __builtin_amdgcn_readfirstlane(lds_addr(st + BM * ROWB + (i * ROWS_PER_LD + wave_row) * ROWB)));
     }
+  }
+
+  __device__ inline void issue(int kb, char* st, bool valid) const {
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) issue_one(kb, st, valid, j);
   }
 
   // The K block that runs past the contraction end, through registers: chunks
@@ -277,11 +266,11 @@ struct MainLoop {
     const int r32 = lane & 31, h = lane >> 5;
     const char* a_row0 = st + (wr * 128 + r32) * ROWB;
     const char* b_row0 = st + BM * ROWB + (wc * (BN / WC) + r32) * ROWB;
-    const int ch = ((2 * s + h) ^ ((r32 >> 2) & 3)) << 4;
-#pragma unroll
-    for (int bi = 0; bi < 4; ++bi) f.a[bi] = *reinterpret_cast<const uint4*>(a_row0 + bi * 32 * ROWB + ch);
+    const int ch = ((2 * s + h) ^ ((r32 >> 1) & 7)) << 4;
 #pragma unroll
     for (int bj = 0; bj < NBJ; ++bj) f.b[bj] = *reinterpret_cast<const uint4*>(b_row0 + bj * 32 * ROWB + ch);
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi) f.a[bi] = *reinterpret_cast<const uint4*>(a_row0 + bi * 32 * ROWB + ch);
   }
 
   __device__ inline static void mma(const Frags& f, f32x16 (&acc)[4][NBJ]) {
@@ -291,33 +280,12 @@ struct MainLoop {
       for (int bj = 0; bj < NBJ; ++bj) mma_block<T>(f.a[bi], f.b[bj], acc[bi][bj]);
   }
 
-  // Multiplies the K block staged in `cur` whose first-substep fragments are
-  // already in f0.  Interleaved with the MFMAs: `issue_next` (loads of a later
-  // K block) and the second substep's fragments during the first substep, and
-  // the first-substep fragments of the next block (stage `pre`) during the
-  // second, so no LDS latency is exposed after the next barrier.
-  template <class F>
-  __device__ inline static void compute(const char* cur, const char* pre, Frags& f0,
-                                        f32x16 (&acc)[4][NBJ], F&& issue_one) {
-    Frags f1;
-    load(cur, 1, f1);
-    int j = 0;
-#pragma unroll
-    for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-      for (int bj = 0; bj < NBJ; ++bj) {
-        mma_block<T>(f0.a[bi], f0.b[bj], acc[bi][bj]);
-        if (j < LOADS) issue_one(j);  // one load of a later K block per MFMA
-        ++j;
-      }
-#pragma unroll
-    for (int g = 0; g < 4 + NBJ; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    load(pre, 0, f0);
-    mma(f1, acc);
+  // One substep: MFMAs on `cur` while the fragments of the next substep are
+  // read into `nxt` (one LDS read after each MFMA).
+  __device__ inline static void substep(const char* st, int s_next, const Frags& cur, Frags& nxt,
+                                        f32x16 (&acc)[4][NBJ]) {
+    load(st, s_next, nxt);
+    mma(cur, acc);
 #pragma unroll
     for (int g = 0; g < 4 + NBJ; ++g) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -334,31 +302,56 @@ __device__ inline void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
 }
 
+// s_waitcnt vmcnt(0) lgkmcnt(0).
+__device__ inline void wait_vm_lgkm() { __builtin_amdgcn_s_waitcnt(0x0070); }
+
 template <typename T, int BN, int WC>
 struct KLoop {
   using ML = MainLoop<T, BN, WC>;
   ML ml;
   int kb_full;
-  typename ML::Frags f0;  // first-substep fragments of the block about to be multiplied
+  typename ML::Frags fa;  // substep-0 fragments of the block about to be multiplied
 
-  // Multiplies K block kb (stage `cur`, fragments of its first substep in f0),
-  // prefetches the first-substep fragments of block kb+1 (stage `pre`) and
-  // issues block kb+3 into `nxt` (the stage of block kb-1).  Before the
-  // barrier each wavefront waits until only block kb+2's loads may still be in
-  // flight, i.e. its loads of kb+1 have landed; the barrier (without a memory
-  // fence, which would wait for everything) then publishes kb+1 and retires
-  // every wavefront's reads of kb-1.
-  __device__ inline void step(int kb, char* cur, char* pre, char* nxt, f32x16 (&acc)[4][ML::NBJ]) {
-    wait_vmcnt<ML::LOADS>();
+  // Multiplies K block kb held in stage `cur` (fa: its substep-0 fragments).
+  // Substeps 0..2 each read the next substep's fragments.  Before the last
+  // substep every wavefront waits for its loads of kb+1 and for its own LDS
+  // reads; the barrier (without a memory fence, which would wait for
+  // everything) then publishes kb+1 and retires every read of `cur`.  The
+  // last substep's MFMAs overlap the substep-0 reads of kb+1 (stage `oth`)
+  // and the loads of kb+2 into `cur`.
+  __device__ inline void step(int kb, char* cur, char* oth, f32x16 (&acc)[4][ML::NBJ]) {
+    static_assert(ML::SUB == 4, "four substeps per K block");
+    typename ML::Frags fb;
+    ML::substep(cur, 1, fa, fb, acc);
+    ML::substep(cur, 2, fb, fa, acc);
+    ML::substep(cur, 3, fa, fb, acc);
+    wait_vm_lgkm();
     __builtin_amdgcn_s_barrier();
-    const bool valid = kb + 3 < kb_full;
-    ML::compute(cur, pre, f0, acc, [&](int j) { ml.issue_one(kb + 3, nxt, valid, j); });
+    const bool valid = kb + 2 < kb_full;
+    ML::load(oth, 0, fa);
+    int j = 0;
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < ML::NBJ; ++bj) {
+        mma_block<T>(fb.a[bi], fb.b[bj], acc[bi][bj]);
+        if (j < ML::LOADS) ml.issue_one(kb + 2, cur, valid, j);  // one load per MFMA block
+        ++j;
+      }
+#pragma unroll
+    for (; j < ML::LOADS; ++j) ml.issue_one(kb + 2, cur, valid, j);
+#pragma unroll
+    for (int g = 0; g < 4 + ML::NBJ; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 };
 
 template <typename T, int BN, int WC>
 __device__ inline void gemm_mainloop(const Operand& A, const Operand& B, int k_elems, int tm, int tn,
-                                     int kb0, int kb1, char* st0, char* st1, char* st2, char* st3,
+                                     int kb0, int kb1, char* st0, char* st1,
                                      f32x16 (&acc)[4][BN / (32 * WC)]) {
   using ML = MainLoop<T, BN, WC>;
 #pragma unroll
@@ -373,27 +366,26 @@ __device__ inline void gemm_mainloop(const Operand& A, const Operand& B, int k_e
   const int kb_full = L.kb_full;
   L.ml.issue(kb0 + 0, st0, kb0 + 0 < kb_full);
   L.ml.issue(kb0 + 1, st1, kb0 + 1 < kb_full);
-  L.ml.issue(kb0 + 2, st2, kb0 + 2 < kb_full);
-  wait_vmcnt<2 * ML::LOADS>();  // block kb0 landed
+  wait_vmcnt<ML::LOADS>();  // block kb0 landed
   __builtin_amdgcn_s_barrier();
-  ML::load(st0, 0, L.f0);
+  ML::load(st0, 0, L.fa);
   int kb = kb0;
-  for (; kb + 4 <= kb_full; kb += 4) {
-    L.step(kb + 0, st0, st1, st3, acc);
-    L.step(kb + 1, st1, st2, st0, acc);
-    L.step(kb + 2, st2, st3, st1, acc);
-    L.step(kb + 3, st3, st0, st2, acc);
+  for (; kb + 2 <= kb_full; kb += 2) {
+    L.step(kb + 0, st0, st1, acc);
+    L.step(kb + 1, st1, st0, acc);
   }
-  if (kb + 0 < kb_full) L.step(kb + 0, st0, st1, st3, acc);
-  if (kb + 1 < kb_full) L.step(kb + 1, st1, st2, st0, acc);
-  if (kb + 2 < kb_full) L.step(kb + 2, st2, st3, st1, acc);
+  if (kb < kb_full) L.step(kb, st0, st1, acc);
   wait_vmcnt<0>();      // the trailing out-of-range loads, before LDS is reused
   __syncthreads();
   if (kb_full < kb1) {  // ragged last block (at most one)
-    L.ml.load_ragged(kb_full, st3);
+    L.ml.load_ragged(kb_full, st0);
     __syncthreads();
-    ML::load(st3, 0, L.f0);
-    ML::compute(st3, st3, L.f0, acc, [](int) {});
+    typename ML::Frags f0, f1;
+    ML::load(st0, 0, f0);
+    ML::substep(st0, 1, f0, f1, acc);
+    ML::substep(st0, 2, f1, f0, acc);
+    ML::substep(st0, 3, f0, f1, acc);
+    ML::mma(f1, acc);
     __syncthreads();
   }
 }
@@ -443,7 +435,7 @@ __global__ __launch_bounds__(kFusedThreads, 1) void fwd_gemm_kernel(Operand A, O
   const TileIdx ti = map_tile<4>(tiles_m, tiles_n, 1);
   f32x16 acc[4][NBJ];
   const int kb_end = (k_elems + Traits<T>::BK - 1) / Traits<T>::BK;
-  gemm_mainloop<T, BN, WC>(A, B, k_elems, ti.tm, ti.tn, 0, kb_end, st0, st1, st2, st3, acc);
+  gemm_mainloop<T, BN, WC>(A, B, k_elems, ti.tm, ti.tn, 0, kb_end, st0, st1, acc);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave / WC, wc = wave % WC, r32 = lane & 31, h = lane >> 5;
@@ -480,7 +472,7 @@ __global__ __launch_bounds__(kFusedThreads, 1) void fwd_gemm_kernel(Operand A, O
     tsum[bj] = sm;
   }
   // --- merge the two vocabulary halves (wr = 0, 1) through LDS
-  float2* red = reinterpret_cast<float2*>(st2);
+  float2* red = reinterpret_cast<float2*>(st0);  // reused by the first gather round only after a barrier
   if (h == 0) {
 #pragma unroll
     for (int bj = 0; bj < NBJ; ++bj)
@@ -539,7 +531,7 @@ __global__ __launch_bounds__(kFusedThreads, 1) void recompute_gemm_kernel(Operan
   const TileIdx ti = map_tile<4>(tiles_m, tiles_n, 1);
   f32x16 acc[4][NBJ];
   const int kb_end = (k_elems + Traits<T>::BK - 1) / Traits<T>::BK;
-  gemm_mainloop<T, BN, WC>(A, B, k_elems, ti.tm, ti.tn, 0, kb_end, st0, st1, st2, st3, acc);
+  gemm_mainloop<T, BN, WC>(A, B, k_elems, ti.tm, ti.tn, 0, kb_end, st0, st1, acc);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave / WC, wc = wave % WC, r32 = lane & 31, h = lane >> 5;
@@ -653,7 +645,7 @@ __global__ __launch_bounds__(kPlainThreads, 1) void plain_gemm_kernel(Operand A,
   const int kb0 = ti.split * kb_per_split;
   const int kb1 = min(kb0 + kb_per_split, kb_total);
   f32x16 acc[4][NBJ];
-  gemm_mainloop<T, BN, WC>(A, B, k_elems, ti.tm, ti.tn, kb0, kb1, st0, st1, st2, st3, acc);
+  gemm_mainloop<T, BN, WC>(A, B, k_elems, ti.tm, ti.tn, kb0, kb1, st0, st1, acc);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave / WC, wc = wave % WC, r32 = lane & 31, h = lane >> 5;
@@ -735,7 +727,7 @@ void launch_recompute_gemm(DType t, const void* W, int V, const void* Hc, int ro
 void launch_dh_gemm(DType t, const void* G, int rows, int v_pad, const void* WT, int d, int splits,
                     float* part, long long split_stride, hipStream_t s) {
   const int tiles_m = (rows + BM - 1) / BM, tiles_n = (d + TILE_D - 1) / TILE_D;
-  const int bk = t == DType::BF16 ? Traits<__bf16>::BK : Traits<float>::BK;
+  const int bk = k_block(t);
   const int kb_total = (v_pad + bk - 1) / bk;
   const int kb_per = (kb_total + splits - 1) / splits;
   const int grid = tiles_m * tiles_n * splits;
@@ -752,7 +744,7 @@ void launch_dh_gemm(DType t, const void* G, int rows, int v_pad, const void* WT,
 void launch_dw_gemm(DType t, const void* GT, int V, int c_pad, const void* HT, int d, float* dW,
                     hipStream_t s) {
   const int tiles_m = (V + BM - 1) / BM, tiles_n = (d + TILE_D - 1) / TILE_D;
-  const int bk = t == DType::BF16 ? Traits<__bf16>::BK : Traits<float>::BK;
+  const int bk = k_block(t);
   const int kb_total = (c_pad + bk - 1) / bk;
   const int grid = tiles_m * tiles_n;
   if (t == DType::BF16)

@@ -17,6 +17,7 @@ constexpr int TILE_T = 256;     // token columns per fused-GEMM tile
 constexpr int TILE_D = 256;     // hidden-dim columns per dH / dW tile
 constexpr int ROW_BLOCK = 64;   // chunk starts are multiples of this many rows
 constexpr int KPAD = 64;        // contraction lengths of dH / dW are padded to this
+constexpr int KBLOCK_BYTES = 128;  // bytes of K per staged GEMM row (64 bf16 / 32 fp32)
 
 // Written by the teacher-preparation kernel, read by later kernels.
 struct Ctrl {
@@ -28,6 +29,9 @@ struct Ctrl {
 enum class DType { BF16 = 0, F32 = 1 };
 
 inline size_t elem_size(DType t) { return t == DType::BF16 ? 2 : 4; }
+// K elements per GEMM main-loop block; KPAD is a multiple of it for both types.
+inline int k_block(DType t) { return KBLOCK_BYTES / (int)elem_size(t); }
+static_assert(KPAD % (KBLOCK_BYTES / 2) == 0, "dH / dW contractions must hold whole K blocks");
 
 // ---------------------------------------------------------------- small kernels
 void launch_fill_i32(int* p, long long count, int value, hipStream_t s);
