@@ -81,17 +81,18 @@ __device__ inline void dma16(i32x4 rsrc, unsigned voff, unsigned lds) {
 constexpr int kStgLd = BM + 4;
 constexpr int kStgBytes = 32 * kStgLd * 4;
 
+// LDS of one GEMM workgroup: three K-block slots of A (BM rows) and two of B
+// (BN rows), 128-byte rows; the epilogues reuse it after the K loop.
 template <int BN>
 struct Smem {
-  static constexpr int kStage = (BM + BN) * ROWB;   // one K block of A and B
-  static constexpr int kArray = kStage > kStgBytes ? kStage : kStgBytes;
+  static constexpr int kA = BM * ROWB;               // one A slot
+  static constexpr int kB = BN * ROWB;               // one B slot
+  static constexpr int kBytes = 3 * kA + 2 * kB;
+  static_assert(kBytes >= 2 * kStgBytes + 16 * BN, "epilogue staging must fit");
+  static_assert(kBytes <= 160 * 1024, "LDS of one CU");
 };
 
-// The stage buffers are distinct LDS arrays so the compiler can see that
-// filling one never aliases reads of another.
-#define KD_DECLARE_STAGES(BN)                                                   \
-  __shared__ __attribute__((aligned(16))) char st0[Smem<BN>::kArray];          \
-  __shared__ __attribute__((aligned(16))) char st1[Smem<BN>::kArray]
+#define KD_DECLARE_LDS(BN) __shared__ __attribute__((aligned(16))) char lds[Smem<BN>::kBytes]
 
 struct TileIdx {
   int tm, tn, split;
@@ -209,31 +210,30 @@ struct MainLoop {
     b_step = (unsigned)(ROWS_PER_LD * B.ld);
   }
 
-  // Load instruction j (0 <= j < LOADS) of the full K block kb into stage
-  // `st`: j < A_LD are A rows, the rest B rows.  With valid == false every
-  // lane is out of range: the instruction still counts in vmcnt (so every
-  // step waits for the same count) but reads nothing.
-  __device__ inline void issue_one(int kb, char* st, bool valid, int j) const {
-    const unsigned koff = (unsigned)kb * ROWB;
-    if (j < A_LD) {
-      const int i = j;
-      const unsigned off = (valid && wave_row + r + ROWS_PER_LD * i < a_valid) ? a_off + i * a_step + koff : kOut;
-      dma16(ra, off, __builtin_amdgcn_readfirstlane(lds_addr(st + (i * ROWS_PER_LD + wave_row) * ROWB)));
-    } else {
-      const int i = j - A_LD;
-      const unsigned off = (valid && wave_row + r + ROWS_PER_LD * i < b_valid) ? b_off + i * b_step + koff : kOut;
-      dma16(rb, off, __builtin_amdgcn_readfirstlane(lds_addr(st + BM * ROWB + (i * ROWS_PER_LD + wave_row) * ROWB)));
-    }
+  // Load instruction i of the full K block kb into the A slot `st` (i < A_LD)
+  // or the B slot (i < B_LD).  With valid == false every lane is out of
+  // range: the instruction still counts in vmcnt (so every step waits for the
+  // same count) but reads nothing.
+  __device__ inline void issue_a(int kb, char* st, bool valid, int i) const {
+    const unsigned off = (valid && wave_row + r + ROWS_PER_LD * i < a_valid) ? a_off + i * a_step + (unsigned)kb * ROWB : kOut;
+    dma16(ra, off, __builtin_amdgcn_readfirstlane(lds_addr(st + (i * ROWS_PER_LD + wave_row) * ROWB)));
   }
-
-  __device__ inline void issue(int kb, char* st, bool valid) const {
+  __device__ inline void issue_b(int kb, char* st, bool valid, int i) const {
+    const unsigned off = (valid && wave_row + r + ROWS_PER_LD * i < b_valid) ? b_off + i * b_step + (unsigned)kb * ROWB : kOut;
+    dma16(rb, off, __builtin_amdgcn_readfirstlane(lds_addr(st + (i * ROWS_PER_LD + wave_row) * ROWB)));
+  }
+  __device__ inline void issue_all_a(int kb, char* st, bool valid) const {
 #pragma unroll
-    for (int j = 0; j < LOADS; ++j) issue_one(kb, st, valid, j);
+    for (int i = 0; i < A_LD; ++i) issue_a(kb, st, valid, i);
+  }
+  __device__ inline void issue_all_b(int kb, char* st, bool valid) const {
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) issue_b(kb, st, valid, i);
   }
 
   // The K block that runs past the contraction end, through registers: chunks
   // at k >= k_elems read as zero (out-of-range offset of an ordinary load).
-  __device__ inline void load_ragged(int kb, char* st) const {
+  __device__ inline void load_ragged(int kb, char* sa, char* sb) const {
     const unsigned koff = (unsigned)kb * ROWB;
     const bool k_ok = kb * BK + c * EPC < k_elems;
     const int lane_pos = (threadIdx.x & 63) * 16;
@@ -245,13 +245,13 @@ struct MainLoop {
     for (int i = 0; i < A_LD; ++i) {
       const unsigned off = (k_ok && wave_row + r + ROWS_PER_LD * i < a_valid) ? a_off + i * a_step + koff : kOut;
       const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ba, off, 0, 0));
-      *reinterpret_cast<uint4*>(st + (i * ROWS_PER_LD + wave_row) * ROWB + lane_pos) = v;
+      *reinterpret_cast<uint4*>(sa + (i * ROWS_PER_LD + wave_row) * ROWB + lane_pos) = v;
     }
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
       const unsigned off = (k_ok && wave_row + r + ROWS_PER_LD * i < b_valid) ? b_off + i * b_step + koff : kOut;
       const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(bb, off, 0, 0));
-      *reinterpret_cast<uint4*>(st + BM * ROWB + (i * ROWS_PER_LD + wave_row) * ROWB + lane_pos) = v;
+      *reinterpret_cast<uint4*>(sb + (i * ROWS_PER_LD + wave_row) * ROWB + lane_pos) = v;
     }
   }
 
@@ -259,13 +259,14 @@ struct MainLoop {
     uint4 a[4], b[NBJ];
   };
 
-  // Fragment loads of substep s (16 bf16 / 8 fp32 K elements) from stage `st`.
-  __device__ inline static void load(const char* st, int s, Frags& f) {
+  // Fragment loads of substep s (16 bf16 / 8 fp32 K elements) from the slots
+  // sa (A) and sb (B).
+  __device__ inline static void load(const char* sa, const char* sb, int s, Frags& f) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wr = wave / WC, wc = wave % WC;
     const int r32 = lane & 31, h = lane >> 5;
-    const char* a_row0 = st + (wr * 128 + r32) * ROWB;
-    const char* b_row0 = st + BM * ROWB + (wc * (BN / WC) + r32) * ROWB;
+    const char* a_row0 = sa + (wr * 128 + r32) * ROWB;
+    const char* b_row0 = sb + (wc * (BN / WC) + r32) * ROWB;
     const int ch = ((2 * s + h) ^ ((r32 >> 1) & 7)) << 4;
 #pragma unroll
     for (int bj = 0; bj < NBJ; ++bj) f.b[bj] = *reinterpret_cast<const uint4*>(b_row0 + bj * 32 * ROWB + ch);
@@ -282,9 +283,9 @@ struct MainLoop {
 
   // One substep: MFMAs on `cur` while the fragments of the next substep are
   // read into `nxt` (one LDS read after each MFMA).
-  __device__ inline static void substep(const char* st, int s_next, const Frags& cur, Frags& nxt,
-                                        f32x16 (&acc)[4][NBJ]) {
-    load(st, s_next, nxt);
+  __device__ inline static void substep(const char* sa, const char* sb, int s_next, const Frags& cur,
+                                        Frags& nxt, f32x16 (&acc)[4][NBJ]) {
+    load(sa, sb, s_next, nxt);
     mma(cur, acc);
 #pragma unroll
     for (int g = 0; g < 4 + NBJ; ++g) {
@@ -302,44 +303,68 @@ __device__ inline void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
 }
 
-// s_waitcnt vmcnt(0) lgkmcnt(0).
-__device__ inline void wait_vm_lgkm() { __builtin_amdgcn_s_waitcnt(0x0070); }
+// s_waitcnt vmcnt(n) lgkmcnt(0).
+template <int N>
+__device__ inline void wait_vmcnt_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70);
+}
+
+// K-block slots: block j's A lives in A slot j % 3, its B in B slot j % 2.
+// A is loaded two blocks ahead and B one block ahead, so about one and a half
+// blocks are in flight while one is multiplied.
+template <int BN>
+struct Slots {
+  char* lds;
+  __device__ inline char* a(int i) const { return lds + i * Smem<BN>::kA; }
+  __device__ inline char* b(int i) const { return lds + 3 * Smem<BN>::kA + i * Smem<BN>::kB; }
+};
 
 template <typename T, int BN, int WC>
 struct KLoop {
   using ML = MainLoop<T, BN, WC>;
   ML ml;
+  Slots<BN> sl;
   int kb_full;
   typename ML::Frags fa;  // substep-0 fragments of the block about to be multiplied
 
-  // Multiplies K block kb held in stage `cur` (fa: its substep-0 fragments).
-  // Substeps 0..2 each read the next substep's fragments.  Before the last
-  // substep every wavefront waits for its loads of kb+1 and for its own LDS
-  // reads; the barrier (without a memory fence, which would wait for
-  // everything) then publishes kb+1 and retires every read of `cur`.  The
-  // last substep's MFMAs overlap the substep-0 reads of kb+1 (stage `oth`)
-  // and the loads of kb+2 into `cur`.
-  __device__ inline void step(int kb, char* cur, char* oth, f32x16 (&acc)[4][ML::NBJ]) {
+  // Multiplies K block j (slot phase t = j - kb0 mod 6, fa: its substep-0
+  // fragments).  Substeps 0..2 each read the next substep's fragments.
+  // Before the last substep every wavefront waits until its loads of block
+  // j+1 have landed (only A of j+2 may still be in flight) and its own LDS
+  // reads are done; the barrier (without a memory fence, which would wait for
+  // everything) then publishes j+1 and frees block j's slots.  The last
+  // substep's MFMAs overlap the substep-0 reads of j+1 and the loads of B of
+  // j+2 and A of j+3 into the freed slots.
+  template <int t>
+  __device__ inline void step(int j, f32x16 (&acc)[4][ML::NBJ]) {
     static_assert(ML::SUB == 4, "four substeps per K block");
+    char* const ca = sl.a(t % 3);
+    char* const cb = sl.b(t % 2);
     typename ML::Frags fb;
-    ML::substep(cur, 1, fa, fb, acc);
-    ML::substep(cur, 2, fb, fa, acc);
-    ML::substep(cur, 3, fa, fb, acc);
-    wait_vm_lgkm();
+    ML::substep(ca, cb, 1, fa, fb, acc);
+    ML::substep(ca, cb, 2, fb, fa, acc);
+    ML::substep(ca, cb, 3, fa, fb, acc);
+    wait_vmcnt_lgkm0<ML::A_LD>();
     __builtin_amdgcn_s_barrier();
-    const bool valid = kb + 2 < kb_full;
-    ML::load(oth, 0, fa);
-    int j = 0;
+    const bool vb = j + 2 < kb_full, va = j + 3 < kb_full;
+    ML::load(sl.a((t + 1) % 3), sl.b((t + 1) % 2), 0, fa);
+    int q = 0;
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
       for (int bj = 0; bj < ML::NBJ; ++bj) {
         mma_block<T>(fb.a[bi], fb.b[bj], acc[bi][bj]);
-        if (j < ML::LOADS) ml.issue_one(kb + 2, cur, valid, j);  // one load per MFMA block
-        ++j;
+        // one load per MFMA block: B of j+2 first, then A of j+3
+        if (q < ML::B_LD) ml.issue_b(j + 2, cb, vb, q);
+        else if (q < ML::LOADS) ml.issue_a(j + 3, ca, va, q - ML::B_LD);
+        ++q;
       }
 #pragma unroll
-    for (; j < ML::LOADS; ++j) ml.issue_one(kb + 2, cur, valid, j);
+    for (; q < ML::LOADS; ++q) {
+      if (q < ML::B_LD) ml.issue_b(j + 2, cb, vb, q);
+      else ml.issue_a(j + 3, ca, va, q - ML::B_LD);
+    }
 #pragma unroll
     for (int g = 0; g < 4 + ML::NBJ; ++g) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -351,7 +376,7 @@ struct KLoop {
 
 template <typename T, int BN, int WC>
 __device__ inline void gemm_mainloop(const Operand& A, const Operand& B, int k_elems, int tm, int tn,
-                                     int kb0, int kb1, char* st0, char* st1,
+                                     int kb0, int kb1, char* lds,
                                      f32x16 (&acc)[4][BN / (32 * WC)]) {
   using ML = MainLoop<T, BN, WC>;
 #pragma unroll
@@ -361,30 +386,45 @@ __device__ inline void gemm_mainloop(const Operand& A, const Operand& B, int k_e
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[bi][bj][e] = 0.f;
   KLoop<T, BN, WC> L;
+  L.sl.lds = lds;
   L.ml.init(A, B, k_elems, tm, tn);
   L.kb_full = min(kb1, k_elems / ML::BK);  // blocks entirely inside the contraction
   const int kb_full = L.kb_full;
-  L.ml.issue(kb0 + 0, st0, kb0 + 0 < kb_full);
-  L.ml.issue(kb0 + 1, st1, kb0 + 1 < kb_full);
-  wait_vmcnt<ML::LOADS>();  // block kb0 landed
+  // Same issue order as the steady state: ..., A(j), B(j), A(j+1), B(j+1), A(j+2).
+  L.ml.issue_all_a(kb0 + 0, L.sl.a(0), kb0 + 0 < kb_full);
+  L.ml.issue_all_b(kb0 + 0, L.sl.b(0), kb0 + 0 < kb_full);
+  L.ml.issue_all_a(kb0 + 1, L.sl.a(1), kb0 + 1 < kb_full);
+  L.ml.issue_all_b(kb0 + 1, L.sl.b(1), kb0 + 1 < kb_full);
+  L.ml.issue_all_a(kb0 + 2, L.sl.a(2), kb0 + 2 < kb_full);
+  wait_vmcnt<2 * ML::A_LD + ML::B_LD>();  // block kb0 landed
   __builtin_amdgcn_s_barrier();
-  ML::load(st0, 0, L.fa);
+  ML::load(L.sl.a(0), L.sl.b(0), 0, L.fa);
   int kb = kb0;
-  for (; kb + 2 <= kb_full; kb += 2) {
-    L.step(kb + 0, st0, st1, acc);
-    L.step(kb + 1, st1, st0, acc);
+  for (; kb + 6 <= kb_full; kb += 6) {
+    L.template step<0>(kb + 0, acc);
+    L.template step<1>(kb + 1, acc);
+    L.template step<2>(kb + 2, acc);
+    L.template step<3>(kb + 3, acc);
+    L.template step<4>(kb + 4, acc);
+    L.template step<5>(kb + 5, acc);
   }
-  if (kb < kb_full) L.step(kb, st0, st1, acc);
+  if (kb + 0 < kb_full) L.template step<0>(kb + 0, acc);
+  if (kb + 1 < kb_full) L.template step<1>(kb + 1, acc);
+  if (kb + 2 < kb_full) L.template step<2>(kb + 2, acc);
+  if (kb + 3 < kb_full) L.template step<3>(kb + 3, acc);
+  if (kb + 4 < kb_full) L.template step<4>(kb + 4, acc);
   wait_vmcnt<0>();      // the trailing out-of-range loads, before LDS is reused
   __syncthreads();
   if (kb_full < kb1) {  // ragged last block (at most one)
-    L.ml.load_ragged(kb_full, st0);
+    char* const sa = L.sl.a(0);
+    char* const sb = L.sl.b(0);
+    L.ml.load_ragged(kb_full, sa, sb);
     __syncthreads();
     typename ML::Frags f0, f1;
-    ML::load(st0, 0, f0);
-    ML::substep(st0, 1, f0, f1, acc);
-    ML::substep(st0, 2, f1, f0, acc);
-    ML::substep(st0, 3, f0, f1, acc);
+    ML::load(sa, sb, 0, f0);
+    ML::substep(sa, sb, 1, f0, f1, acc);
+    ML::substep(sa, sb, 2, f1, f0, acc);
+    ML::substep(sa, sb, 3, f0, f1, acc);
     ML::mma(f1, acc);
     __syncthreads();
   }
@@ -395,7 +435,7 @@ __device__ inline void gemm_mainloop(const Operand& A, const Operand& B, int k_e
 // rows [128 wr, +128) and tokens [wc * 256/kFusedWC, +256/kFusedWC) of the tile,
 // i.e. NBJ 32-token MFMA blocks.  Token block tb = wc * NBJ + bj covers tokens
 // [32 tb, +32).  The LDS-staged epilogue works in 4 rounds of 64 contiguous
-// tokens: round r stages token blocks 2r (in st0) and 2r+1 (in st1).
+// tokens: round r stages token blocks 2r (in stg0) and 2r+1 (in stg1).
 #ifndef KD_FUSED_WC
 #define KD_FUSED_WC 4
 #endif
@@ -431,11 +471,11 @@ __global__ __launch_bounds__(kFusedThreads, 1) void fwd_gemm_kernel(Operand A, O
                                                                      int tiles_m, int tiles_n,
                                                                      FwdEpilogue ep) {
   constexpr int BN = 256, NBJ = kFusedNBJ, WC = kFusedWC;
-  KD_DECLARE_STAGES(BN);
+  KD_DECLARE_LDS(BN);
   const TileIdx ti = map_tile<4>(tiles_m, tiles_n, 1);
   f32x16 acc[4][NBJ];
   const int kb_end = (k_elems + Traits<T>::BK - 1) / Traits<T>::BK;
-  gemm_mainloop<T, BN, WC>(A, B, k_elems, ti.tm, ti.tn, 0, kb_end, st0, st1, acc);
+  gemm_mainloop<T, BN, WC>(A, B, k_elems, ti.tm, ti.tn, 0, kb_end, lds, acc);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave / WC, wc = wave % WC, r32 = lane & 31, h = lane >> 5;
@@ -472,7 +512,7 @@ __global__ __launch_bounds__(kFusedThreads, 1) void fwd_gemm_kernel(Operand A, O
     tsum[bj] = sm;
   }
   // --- merge the two vocabulary halves (wr = 0, 1) through LDS
-  float2* red = reinterpret_cast<float2*>(st0);  // reused by the first gather round only after a barrier
+  float2* red = reinterpret_cast<float2*>(lds + 2 * kStgBytes);
   if (h == 0) {
 #pragma unroll
     for (int bj = 0; bj < NBJ; ++bj)
@@ -498,8 +538,8 @@ __global__ __launch_bounds__(kFusedThreads, 1) void fwd_gemm_kernel(Operand A, O
   const int h_lo = ep.hit_off[key0 + row_lo / ROW_BLOCK];
   const int h_hi = ep.hit_off[key0 + (row_hi + ROW_BLOCK - 1) / ROW_BLOCK];
   if (h_lo >= h_hi) return;  // uniform over the workgroup
-  float* const stg0 = reinterpret_cast<float*>(st0);
-  float* const stg1 = reinterpret_cast<float*>(st1);
+  float* const stg0 = reinterpret_cast<float*>(lds);
+  float* const stg1 = reinterpret_cast<float*>(lds + kStgBytes);
 #pragma unroll
   for (int round = 0; round < 4; ++round) {
     __syncthreads();
@@ -527,11 +567,11 @@ __global__ __launch_bounds__(kFusedThreads, 1) void recompute_gemm_kernel(Operan
                                                                            int tiles_n,
                                                                            RecomputeEpilogue ep) {
   constexpr int BN = 256, NBJ = kFusedNBJ, WC = kFusedWC;
-  KD_DECLARE_STAGES(BN);
+  KD_DECLARE_LDS(BN);
   const TileIdx ti = map_tile<4>(tiles_m, tiles_n, 1);
   f32x16 acc[4][NBJ];
   const int kb_end = (k_elems + Traits<T>::BK - 1) / Traits<T>::BK;
-  gemm_mainloop<T, BN, WC>(A, B, k_elems, ti.tm, ti.tn, 0, kb_end, st0, st1, acc);
+  gemm_mainloop<T, BN, WC>(A, B, k_elems, ti.tm, ti.tn, 0, kb_end, lds, acc);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave / WC, wc = wave % WC, r32 = lane & 31, h = lane >> 5;
@@ -562,8 +602,8 @@ __global__ __launch_bounds__(kFusedThreads, 1) void recompute_gemm_kernel(Operan
   const int key0 = ti.tm * ep.n_rb;
   const int h_lo = row_lo < row_hi ? ep.hit_off[key0 + row_lo / ROW_BLOCK] : 0;
   const int h_hi = row_lo < row_hi ? ep.hit_off[key0 + (row_hi + ROW_BLOCK - 1) / ROW_BLOCK] : 0;
-  float* const stg0 = reinterpret_cast<float*>(st0);
-  float* const stg1 = reinterpret_cast<float*>(st1);
+  float* const stg0 = reinterpret_cast<float*>(lds);
+  float* const stg1 = reinterpret_cast<float*>(lds + kStgBytes);
   T* G = static_cast<T*>(ep.G);
   T* GT = static_cast<T*>(ep.GT);
   constexpr int EPC = 16 / sizeof(T);
@@ -639,13 +679,13 @@ __global__ __launch_bounds__(kPlainThreads, 1) void plain_gemm_kernel(Operand A,
                                                                        long long split_stride, int M,
                                                                        int N) {
   constexpr int BN = TILE_D, WC = kPlainWC, NBJ = BN / (32 * WC);
-  KD_DECLARE_STAGES(BN);
+  KD_DECLARE_LDS(BN);
   const TileIdx ti = map_tile<8>(tiles_m, tiles_n, splits);
   const int kb_total = (k_elems + Traits<T>::BK - 1) / Traits<T>::BK;
   const int kb0 = ti.split * kb_per_split;
   const int kb1 = min(kb0 + kb_per_split, kb_total);
   f32x16 acc[4][NBJ];
-  gemm_mainloop<T, BN, WC>(A, B, k_elems, ti.tm, ti.tn, kb0, kb1, st0, st1, acc);
+  gemm_mainloop<T, BN, WC>(A, B, k_elems, ti.tm, ti.tn, kb0, kb1, lds, acc);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave / WC, wc = wave % WC, r32 = lane & 31, h = lane >> 5;
