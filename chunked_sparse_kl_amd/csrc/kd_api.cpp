@@ -193,7 +193,7 @@ Layout make_layout(DType dt, int64_t n, int64_t d, int64_t V, int64_t K, int64_t
   L.offs = take(size_t(L.n_keys + 1) * 4);
   L.cursor = take(size_t(L.n_keys) * 4);
   L.scan_tmp = take(size_t(L.scan_tiles + 1) * 4);
-  L.hits = take(size_t(n) * K * 8);
+  L.hits = take(size_t(n) * K * sizeof(kd::Hit));
   L.common_end = o;
   // forward-only region
   L.part = take(size_t(L.n_vt) * chunk * 8);
@@ -328,9 +328,9 @@ int prepare_teacher(const Layout& L, const int32_t* idx, const float* logp, cons
                             reinterpret_cast<int*>(ws + L.cursor),
                             reinterpret_cast<int*>(ws + L.scan_tmp), s));
   KD_LAUNCH("hit_scatter", 0, nk * 12,
-            kd::launch_hit_scatter(idx, mask, n, K, V, (int)L.n_rb,
-                                   reinterpret_cast<int*>(ws + L.cursor),
-                                   reinterpret_cast<int2*>(ws + L.hits), s));
+            kd::launch_hit_scatter(idx, reinterpret_cast<const float*>(ws + L.p), mask, n, K, V,
+                                   (int)L.n_rb, reinterpret_cast<int*>(ws + L.cursor),
+                                   reinterpret_cast<kd::Hit*>(ws + L.hits), s));
   return KD_OK;
 }
 
@@ -434,8 +434,7 @@ int kd_fused_chunked_kl_fwd(int dtype, const void* H, const void* W, const int32
     ep.K = (int)L.K;
     ep.n_rb = (int)L.n_rb;
     ep.hit_off = reinterpret_cast<const int*>(ws + L.offs);
-    ep.hits = reinterpret_cast<const int2*>(ws + L.hits);
-    ep.idx = topk_idx;
+    ep.hits = reinterpret_cast<const kd::Hit*>(ws + L.hits);
     ep.g = g;
     const char* Hc = static_cast<const char*>(H) + c0 * L.d * es;
     const double fl = 2.0 * rows * L.d * L.V;
@@ -491,9 +490,7 @@ int kd_fused_chunked_kl_bwd(int dtype, const void* H, const void* W, const int32
     ep.K = (int)L.K;
     ep.n_rb = (int)L.n_rb;
     ep.hit_off = reinterpret_cast<const int*>(ws + L.offs);
-    ep.hits = reinterpret_cast<const int2*>(ws + L.hits);
-    ep.idx = topk_idx;
-    ep.p = reinterpret_cast<const float*>(ws + L.p);
+    ep.hits = reinterpret_cast<const kd::Hit*>(ws + L.hits);
     ep.S = reinterpret_cast<const float*>(ws + L.S);
     ep.lse = lse;
     ep.mask = mask;

@@ -75,12 +75,6 @@ __device__ inline void dma16(i32x4 rsrc, unsigned voff, unsigned lds) {
 }
 #pragma clang diagnostic pop
 
-// LDS staging of epilogue values: 64 token slots x 256 vocab entries (fp32),
-// row pitch padded to keep the 16-byte stores conflict free; the 32 slots of
-// one wavefront column live in one stage array.
-constexpr int kStgLd = BM + 4;
-constexpr int kStgBytes = 32 * kStgLd * 4;
-
 // LDS of one GEMM workgroup: three K-block slots of A (BM rows) and two of B
 // (BN rows), 128-byte rows; the epilogues reuse it after the K loop.
 template <int BN>
@@ -88,7 +82,6 @@ struct Smem {
   static constexpr int kA = BM * ROWB;               // one A slot
   static constexpr int kB = BN * ROWB;               // one B slot
   static constexpr int kBytes = 3 * kA + 2 * kB;
-  static_assert(kBytes >= 2 * kStgBytes + 16 * BN, "epilogue staging must fit");
   static_assert(kBytes <= 160 * 1024, "LDS of one CU");
 };
 
@@ -430,42 +423,119 @@ __device__ inline void gemm_mainloop(const Operand& A, const Operand& B, int k_e
   }
 }
 
-// ------------------------------------------------------------------ fused epilogue layout
-// The fused kernels use 2 x kFusedWC wavefronts; wavefront (wr, wc) owns vocab
-// rows [128 wr, +128) and tokens [wc * 256/kFusedWC, +256/kFusedWC) of the tile,
-// i.e. NBJ 32-token MFMA blocks.  Token block tb = wc * NBJ + bj covers tokens
-// [32 tb, +32).  The LDS-staged epilogue works in 4 rounds of 64 contiguous
-// tokens: round r stages token blocks 2r (in stg0) and 2r+1 (in stg1).
-#ifndef KD_FUSED_WC
-#define KD_FUSED_WC 4
-#endif
-constexpr int kFusedWC = KD_FUSED_WC;
+// ------------------------------------------------------------------ fused epilogues
+// The fused kernels use 8 wavefronts in a 2 x 4 grid; wavefront (wr, wc) owns
+// vocabulary rows [128 wr, +128) and tokens [64 wc, +64) of the 256 x 256
+// tile as 4 x 2 blocks of 32 x 32.  Its 64 tokens are exactly one 64-row block
+// of the teacher-hit buckets (chunks start at multiples of 64 rows), so each
+// wavefront finds the teacher entries of its tokens in one bucket and applies
+// them to its own accumulators: no workgroup-wide staging, no barriers.
+constexpr int kFusedWC = 4;
 constexpr int kFusedThreads = 128 * kFusedWC;
-constexpr int kFusedNBJ = 256 / (32 * kFusedWC);
+constexpr int kFusedNBJ = 2;
+static_assert(256 / kFusedWC == ROW_BLOCK, "a wavefront's tokens form one hit row block");
 
-// Stages this wavefront's token blocks of round `round` (fp32) into LDS.
-__device__ inline void stage_round(const f32x16 (&acc)[4][kFusedNBJ], int round, int wr, int wc,
-                                   int r32, int h, float* stg0, float* stg1) {
-#pragma unroll
-  for (int bj = 0; bj < kFusedNBJ; ++bj) {
-    const int tb = wc * kFusedNBJ + bj;
-    if ((tb >> 1) != round) continue;  // uniform per wavefront
-    float* stg = (tb & 1) ? stg1 : stg0;
-#pragma unroll
-    for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f32x4 v4 = {acc[bi][bj][4 * i + 0], acc[bi][bj][4 * i + 1], acc[bi][bj][4 * i + 2],
-                    acc[bi][bj][4 * i + 3]};
-        *reinterpret_cast<f32x4*>(stg + r32 * kStgLd + wr * 128 + bi * 32 + 8 * i + 4 * h) = v4;
-      }
+// Register q = 16 * (2 bi + bj) + e of this lane's accumulators (q uniform
+// over the wavefront, so the switch is a scalar branch and the element is
+// picked by register-relative addressing).
+// Accumulator register q = 16 * (2 bi + bj) + e of this lane, q uniform over
+// the wavefront: a switch with constant register indices, i.e. a scalar
+// branch tree (a runtime index would send the accumulators to scratch).
+#define KD_GET(q) \
+  case q:         \
+    return acc[(q) >> 5][((q) >> 4) & 1][(q) & 15];
+#define KD_ADD(q)                               \
+  case q:                                       \
+    acc[(q) >> 5][((q) >> 4) & 1][(q) & 15] += x; \
+    break;
+__device__ inline float acc_get(const f32x16 (&acc)[4][kFusedNBJ], int q) {
+  switch (q) {
+    KD_GET(0) KD_GET(1) KD_GET(2) KD_GET(3) KD_GET(4) KD_GET(5) KD_GET(6) KD_GET(7) KD_GET(8) KD_GET(9) KD_GET(10) KD_GET(11) KD_GET(12) KD_GET(13) KD_GET(14) KD_GET(15)
+    KD_GET(16) KD_GET(17) KD_GET(18) KD_GET(19) KD_GET(20) KD_GET(21) KD_GET(22) KD_GET(23) KD_GET(24) KD_GET(25) KD_GET(26) KD_GET(27) KD_GET(28) KD_GET(29) KD_GET(30) KD_GET(31)
+    KD_GET(32) KD_GET(33) KD_GET(34) KD_GET(35) KD_GET(36) KD_GET(37) KD_GET(38) KD_GET(39) KD_GET(40) KD_GET(41) KD_GET(42) KD_GET(43) KD_GET(44) KD_GET(45) KD_GET(46) KD_GET(47)
+    KD_GET(48) KD_GET(49) KD_GET(50) KD_GET(51) KD_GET(52) KD_GET(53) KD_GET(54) KD_GET(55) KD_GET(56) KD_GET(57) KD_GET(58) KD_GET(59) KD_GET(60) KD_GET(61) KD_GET(62) KD_GET(63)
+    KD_GET(64) KD_GET(65) KD_GET(66) KD_GET(67) KD_GET(68) KD_GET(69) KD_GET(70) KD_GET(71) KD_GET(72) KD_GET(73) KD_GET(74) KD_GET(75) KD_GET(76) KD_GET(77) KD_GET(78) KD_GET(79)
+    KD_GET(80) KD_GET(81) KD_GET(82) KD_GET(83) KD_GET(84) KD_GET(85) KD_GET(86) KD_GET(87) KD_GET(88) KD_GET(89) KD_GET(90) KD_GET(91) KD_GET(92) KD_GET(93) KD_GET(94) KD_GET(95)
+    KD_GET(96) KD_GET(97) KD_GET(98) KD_GET(99) KD_GET(100) KD_GET(101) KD_GET(102) KD_GET(103) KD_GET(104) KD_GET(105) KD_GET(106) KD_GET(107) KD_GET(108) KD_GET(109) KD_GET(110) KD_GET(111)
+    KD_GET(112) KD_GET(113) KD_GET(114) KD_GET(115) KD_GET(116) KD_GET(117) KD_GET(118) KD_GET(119) KD_GET(120) KD_GET(121) KD_GET(122) KD_GET(123) KD_GET(124) KD_GET(125) KD_GET(126) KD_GET(127)
+  }
+  return 0.f;
+}
+
+__device__ inline void acc_add(f32x16 (&acc)[4][kFusedNBJ], int q, float x) {
+  switch (q) {
+    KD_ADD(0) KD_ADD(1) KD_ADD(2) KD_ADD(3) KD_ADD(4) KD_ADD(5) KD_ADD(6) KD_ADD(7) KD_ADD(8) KD_ADD(9) KD_ADD(10) KD_ADD(11) KD_ADD(12) KD_ADD(13) KD_ADD(14) KD_ADD(15)
+    KD_ADD(16) KD_ADD(17) KD_ADD(18) KD_ADD(19) KD_ADD(20) KD_ADD(21) KD_ADD(22) KD_ADD(23) KD_ADD(24) KD_ADD(25) KD_ADD(26) KD_ADD(27) KD_ADD(28) KD_ADD(29) KD_ADD(30) KD_ADD(31)
+    KD_ADD(32) KD_ADD(33) KD_ADD(34) KD_ADD(35) KD_ADD(36) KD_ADD(37) KD_ADD(38) KD_ADD(39) KD_ADD(40) KD_ADD(41) KD_ADD(42) KD_ADD(43) KD_ADD(44) KD_ADD(45) KD_ADD(46) KD_ADD(47)
+    KD_ADD(48) KD_ADD(49) KD_ADD(50) KD_ADD(51) KD_ADD(52) KD_ADD(53) KD_ADD(54) KD_ADD(55) KD_ADD(56) KD_ADD(57) KD_ADD(58) KD_ADD(59) KD_ADD(60) KD_ADD(61) KD_ADD(62) KD_ADD(63)
+    KD_ADD(64) KD_ADD(65) KD_ADD(66) KD_ADD(67) KD_ADD(68) KD_ADD(69) KD_ADD(70) KD_ADD(71) KD_ADD(72) KD_ADD(73) KD_ADD(74) KD_ADD(75) KD_ADD(76) KD_ADD(77) KD_ADD(78) KD_ADD(79)
+    KD_ADD(80) KD_ADD(81) KD_ADD(82) KD_ADD(83) KD_ADD(84) KD_ADD(85) KD_ADD(86) KD_ADD(87) KD_ADD(88) KD_ADD(89) KD_ADD(90) KD_ADD(91) KD_ADD(92) KD_ADD(93) KD_ADD(94) KD_ADD(95)
+    KD_ADD(96) KD_ADD(97) KD_ADD(98) KD_ADD(99) KD_ADD(100) KD_ADD(101) KD_ADD(102) KD_ADD(103) KD_ADD(104) KD_ADD(105) KD_ADD(106) KD_ADD(107) KD_ADD(108) KD_ADD(109) KD_ADD(110) KD_ADD(111)
+    KD_ADD(112) KD_ADD(113) KD_ADD(114) KD_ADD(115) KD_ADD(116) KD_ADD(117) KD_ADD(118) KD_ADD(119) KD_ADD(120) KD_ADD(121) KD_ADD(122) KD_ADD(123) KD_ADD(124) KD_ADD(125) KD_ADD(126) KD_ADD(127)
   }
 }
+#undef KD_GET
+#undef KD_ADD
+
+// The teacher entries of one wavefront: the bucket of (vocabulary tile tm,
+// the 64-row block of its tokens).  The first 64 entries (one per lane) are
+// loaded before the K loop so their latency hides under it.
+struct WaveHits {
+  int lo, hi;      // bucket range in the hit array
+  int row0;        // global row of the wavefront's first token
+  int v_lo;        // first vocabulary id of the wavefront's 128 rows
+  Hit pre;         // this lane's entry among the first 64
+
+  __device__ inline void init(const int* hit_off, const Hit* hits, int n_rb, int tm, int c0, int rows,
+                              int tok0, int v_lo_) {
+    const int lane = threadIdx.x & 63;
+    row0 = c0 + tok0;
+    v_lo = v_lo_;
+    lo = hi = 0;
+    if (tok0 < rows) {  // tokens past the chunk end have no bucket
+      const int key = tm * n_rb + row0 / ROW_BLOCK;
+      lo = hit_off[key];
+      hi = hit_off[key + 1];
+    }
+    pre.row = pre.k = 0;
+    pre.v = -1;
+    pre.p = 0.f;
+    if (lo + lane < hi) pre = hits[lo + lane];
+  }
+
+  // Calls f(q, owner, row, k, p) for each entry whose id falls in the
+  // wavefront's vocabulary rows: accumulator register q of lane `owner`
+  // holds that (token, id) logit.
+  template <class F>
+  __device__ inline void for_each(const Hit* hits, F&& f) const {
+    const int lane = threadIdx.x & 63;
+    for (int base = lo; base < hi; base += 64) {
+      Hit hk = pre;
+      if (base != lo) {
+        hk.v = -1;
+        if (base + lane < hi) hk = hits[base + lane];
+      }
+      const int cnt = min(64, hi - base);
+      for (int u = 0; u < cnt; ++u) {
+        const int vl = __builtin_amdgcn_readlane(hk.v, u) - v_lo;
+        if ((unsigned)vl >= 128u) continue;
+        const int row = __builtin_amdgcn_readlane(hk.row, u);
+        const int k = __builtin_amdgcn_readlane(hk.k, u);
+        const float p = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, hk.p), u));
+        const int tl = row - row0;  // 0..63
+        const int r = vl & 31;
+        const int q = ((((vl >> 5) << 1) | (tl >> 5)) << 4) | ((r >> 3) << 2) | (r & 3);
+        const int owner = (tl & 31) | (((r >> 2) & 1) << 5);
+        f(q, owner, row, k, p);
+      }
+    }
+  }
+};
 
 // ------------------------------------------------------------------ forward
 // D[v][t] = z_{t,v}.  Per token: max and sum of exp(z - max) over this tile's
-// vocabulary rows (-> one (max, sum) partial per vocabulary tile), then the
-// logits at the token's teacher ids are copied out of an LDS-staged slice.
+// vocabulary rows (-> one (max, sum) partial per vocabulary tile); the logits
+// at the token's teacher ids are read straight out of the accumulators.
 template <typename T>
 __global__ __launch_bounds__(kFusedThreads, 1) void fwd_gemm_kernel(Operand A, Operand B, int k_elems,
                                                                      int tiles_m, int tiles_n,
@@ -473,15 +543,24 @@ __global__ __launch_bounds__(kFusedThreads, 1) void fwd_gemm_kernel(Operand A, O
   constexpr int BN = 256, NBJ = kFusedNBJ, WC = kFusedWC;
   KD_DECLARE_LDS(BN);
   const TileIdx ti = map_tile<4>(tiles_m, tiles_n, 1);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave / WC, wc = wave % WC, r32 = lane & 31, h = lane >> 5;
+  WaveHits wh;
+  wh.init(ep.hit_off, ep.hits, ep.n_rb, ti.tm, ep.c0, ep.rows, ti.tn * BN + wc * 64,
+          ti.tm * BM + wr * 128);
   f32x16 acc[4][NBJ];
   const int kb_end = (k_elems + Traits<T>::BK - 1) / Traits<T>::BK;
   gemm_mainloop<T, BN, WC>(A, B, k_elems, ti.tm, ti.tn, 0, kb_end, lds, acc);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wr = wave / WC, wc = wave % WC, r32 = lane & 31, h = lane >> 5;
+  // --- gather the logits at the teacher ids that fall in this wavefront's block
+  wh.for_each(ep.hits, [&](int q, int owner, int row, int k, float) {
+    const float z = acc_get(acc, q);
+    if (lane == owner) ep.g[(long long)row * ep.K + k] = z;
+  });
+
   const int v_base = ti.tm * BM + wr * 128 + 4 * h;  // + bi*32 + 8*i + j
   const bool full_v = (ti.tm + 1) * BM <= ep.V;
-
   // --- per-token (max, sum-exp) over this wavefront's 128 vocabulary rows
   float tmax[NBJ], tsum[NBJ];
 #pragma unroll
@@ -512,7 +591,7 @@ __global__ __launch_bounds__(kFusedThreads, 1) void fwd_gemm_kernel(Operand A, O
     tsum[bj] = sm;
   }
   // --- merge the two vocabulary halves (wr = 0, 1) through LDS
-  float2* red = reinterpret_cast<float2*>(lds + 2 * kStgBytes);
+  float2* red = reinterpret_cast<float2*>(lds);
   if (h == 0) {
 #pragma unroll
     for (int bj = 0; bj < NBJ; ++bj)
@@ -530,37 +609,15 @@ __global__ __launch_bounds__(kFusedThreads, 1) void fwd_gemm_kernel(Operand A, O
       ep.part[(long long)ti.tm * ep.ld_part + n] = make_float2(m, s);
     }
   }
-
-  // --- gather the logits at the teacher ids that fall in this tile
-  const int row_lo = ep.c0 + ti.tn * BN;
-  const int row_hi = ep.c0 + min(ti.tn * BN + BN, ep.rows);
-  const int key0 = ti.tm * ep.n_rb;
-  const int h_lo = ep.hit_off[key0 + row_lo / ROW_BLOCK];
-  const int h_hi = ep.hit_off[key0 + (row_hi + ROW_BLOCK - 1) / ROW_BLOCK];
-  if (h_lo >= h_hi) return;  // uniform over the workgroup
-  float* const stg0 = reinterpret_cast<float*>(lds);
-  float* const stg1 = reinterpret_cast<float*>(lds + kStgBytes);
-#pragma unroll
-  for (int round = 0; round < 4; ++round) {
-    __syncthreads();
-    stage_round(acc, round, wr, wc, r32, h, stg0, stg1);
-    __syncthreads();
-    for (int x = h_lo + tid; x < h_hi; x += kFusedThreads) {
-      const int2 hk = ep.hits[x];
-      const int sl = hk.x - row_lo - round * 64;  // staged slot of the token
-      if (sl < 0 || sl >= 64) continue;
-      const long long gi = (long long)hk.x * ep.K + hk.y;
-      const int vl = ep.idx[gi] - ti.tm * BM;
-      ep.g[gi] = ((sl >> 5) ? stg1 : stg0)[(sl & 31) * kStgLd + vl];
-    }
-  }
 }
 
 // ------------------------------------------------------------------ recompute
 // D[v][t] = z_{t,v} again; G_{t,v} = gw*S_t*q_{t,v} - gw*sum_k p_{t,k}[i_{t,k} = v]
-// with gw = grad_loss * mask_t / N_valid, staged through LDS (fp32) where the
-// scatter is applied, then rounded to T and written row-major (G) and
-// transposed (G^T).
+// with gw = grad_loss * mask_t / N_valid, formed in the accumulators (the
+// scatter goes straight into the owning registers), rounded to T and written
+// transposed (G^T, straight from registers: a lane's 32-token column is
+// contiguous there) and row-major (G, through a per-wavefront LDS block so the
+// stores are whole rows).
 template <typename T>
 __global__ __launch_bounds__(kFusedThreads, 1) void recompute_gemm_kernel(Operand A, Operand B,
                                                                            int k_elems, int tiles_m,
@@ -569,20 +626,23 @@ __global__ __launch_bounds__(kFusedThreads, 1) void recompute_gemm_kernel(Operan
   constexpr int BN = 256, NBJ = kFusedNBJ, WC = kFusedWC;
   KD_DECLARE_LDS(BN);
   const TileIdx ti = map_tile<4>(tiles_m, tiles_n, 1);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave / WC, wc = wave % WC, r32 = lane & 31, h = lane >> 5;
+  const int n_wave = ti.tn * BN + wc * 64;  // chunk-local first token of this wavefront
+  const int v_wave = ti.tm * BM + wr * 128; // first vocabulary row of this wavefront
+  WaveHits wh;
+  wh.init(ep.hit_off, ep.hits, ep.n_rb, ti.tm, ep.c0, ep.rows, n_wave, v_wave);
   f32x16 acc[4][NBJ];
   const int kb_end = (k_elems + Traits<T>::BK - 1) / Traits<T>::BK;
   gemm_mainloop<T, BN, WC>(A, B, k_elems, ti.tm, ti.tn, 0, kb_end, lds, acc);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wr = wave / WC, wc = wave % WC, r32 = lane & 31, h = lane >> 5;
-  const int v_base = ti.tm * BM + wr * 128 + 4 * h;
   const bool full_v = (ti.tm + 1) * BM <= ep.V;
   const int nv = ep.ctrl->n_valid;
   const float gw = nv > 0 ? ep.grad_loss[0] / (float)nv : 0.f;
-
 #pragma unroll
   for (int bj = 0; bj < NBJ; ++bj) {
-    const int n = ti.tn * BN + (wc * NBJ + bj) * 32 + r32;
+    const int n = n_wave + bj * 32 + r32;
     const int t = ep.c0 + n;
     const bool live = n < ep.rows && (ep.mask == nullptr || ep.mask[t] != 0);
     const float coef = live ? gw * ep.S[t] : 0.f;
@@ -591,74 +651,80 @@ __global__ __launch_bounds__(kFusedThreads, 1) void recompute_gemm_kernel(Operan
     for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int v = v_base + bi * 32 + 8 * (e >> 2) + (e & 3);
+        const int v = v_wave + bi * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
         const float q = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[bi][bj][e], kLog2e, -lse2));
         acc[bi][bj][e] = (coef != 0.f && (full_v || v < ep.V)) ? coef * q : 0.f;
       }
   }
+  // Teacher entries: G -= gw * p at (t, i_{t,k}) (masked rows have none).
+  wh.for_each(ep.hits, [&](int q, int owner, int, int, float p) {
+    acc_add(acc, q, lane == owner ? -gw * p : 0.f);
+  });
 
-  const int row_lo = ep.c0 + ti.tn * BN;
-  const int row_hi = ep.c0 + min(ti.tn * BN + BN, ep.rows);
-  const int key0 = ti.tm * ep.n_rb;
-  const int h_lo = row_lo < row_hi ? ep.hit_off[key0 + row_lo / ROW_BLOCK] : 0;
-  const int h_hi = row_lo < row_hi ? ep.hit_off[key0 + (row_hi + ROW_BLOCK - 1) / ROW_BLOCK] : 0;
-  float* const stg0 = reinterpret_cast<float*>(lds);
-  float* const stg1 = reinterpret_cast<float*>(lds + kStgBytes);
   T* G = static_cast<T*>(ep.G);
   T* GT = static_cast<T*>(ep.GT);
-  constexpr int EPC = 16 / sizeof(T);
-
+  // --- G^T[v][n]: for a fixed register, the 32 lanes of a half-wavefront
+  // hold 32 consecutive tokens of one vocabulary row.  bf16: neighbouring
+  // lanes swap values so each lane stores two tokens (4 bytes).
 #pragma unroll
-  for (int round = 0; round < 4; ++round) {
-    __syncthreads();
-    stage_round(acc, round, wr, wc, r32, h, stg0, stg1);
-    __syncthreads();
-    for (int x = h_lo + tid; x < h_hi; x += kFusedThreads) {
-      const int2 hk = ep.hits[x];
-      const int sl = hk.x - row_lo - round * 64;
-      if (sl < 0 || sl >= 64) continue;
-      const long long gi = (long long)hk.x * ep.K + hk.y;
-      const int vl = ep.idx[gi] - ti.tm * BM;
-      atomicAdd(&((sl >> 5) ? stg1 : stg0)[(sl & 31) * kStgLd + vl], -gw * ep.p[gi]);
-    }
-    __syncthreads();
-    const int n_round = ti.tn * BN + round * 64;  // first token of the round
-    // G rows: 64 tokens x 256 vocab, EPC elements per 16-byte store.
-    constexpr int kRowChunks = BM / EPC;
+  for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-    for (int it = 0; it < 64 * kRowChunks / kFusedThreads; ++it) {
-      const int q = it * kFusedThreads + tid;
-      const int slot = q / kRowChunks, c = q % kRowChunks;
-      const int n = n_round + slot;
-      const int v0 = ti.tm * BM + c * EPC;
-      if (n < ep.c_pad && v0 < ep.v_pad) {
-        const float* src = ((slot >> 5) ? stg1 : stg0) + (slot & 31) * kStgLd + c * EPC;
-        T tmp[EPC];
+    for (int bj = 0; bj < NBJ; ++bj) {
+      const int n = n_wave + bj * 32 + r32;
 #pragma unroll
-        for (int u = 0; u < EPC; ++u) tmp[u] = (T)src[u];
-        *reinterpret_cast<uint4*>(G + (long long)n * ep.v_pad + v0) =
-            *reinterpret_cast<const uint4*>(tmp);
-      }
-    }
-    // G^T rows: 256 vocab x 64 contiguous tokens, EPC tokens per store.
-    constexpr int kTokChunks = 64 / EPC;
+      for (int i = 0; i < 4; ++i) {
+        const int v0 = v_wave + bi * 32 + 8 * i + 4 * h;
+        if constexpr (sizeof(T) == 2) {
 #pragma unroll
-    for (int it = 0; it < BM * kTokChunks / kFusedThreads; ++it) {
-      const int q = it * kFusedThreads + tid;
-      const int vl = q & (BM - 1);
-      const int cq = q / BM;
-      const int v = ti.tm * BM + vl;
-      const int n0 = n_round + cq * EPC;
-      if (v < ep.v_pad && n0 < ep.c_pad) {
-        T tmp[EPC];
+          for (int jp = 0; jp < 2; ++jp) {
+            const float x0 = acc[bi][bj][4 * i + 2 * jp], x1 = acc[bi][bj][4 * i + 2 * jp + 1];
+            const float y0 = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x0), 0xB1, 0xF, 0xF, true));
+            const float y1 = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x1), 0xB1, 0xF, 0xF, true));
+            const bool odd = (lane & 1) != 0;
+            const int v = v0 + 2 * jp + (odd ? 1 : 0);
+            const int n2 = n & ~1;
+            T pr[2] = {(T)(odd ? y1 : x0), (T)(odd ? x1 : y0)};
+            if (v < ep.v_pad && n2 < ep.c_pad)
+              *reinterpret_cast<uint32_t*>(GT + (long long)v * ep.c_pad + n2) =
+                  *reinterpret_cast<const uint32_t*>(pr);
+          }
+        } else {
 #pragma unroll
-        for (int u = 0; u < EPC; ++u) {
-          const int sl = cq * EPC + u;
-          tmp[u] = (T)((sl >> 5) ? stg1 : stg0)[(sl & 31) * kStgLd + vl];
+          for (int j = 0; j < 4; ++j)
+            if (v0 + j < ep.v_pad && n < ep.c_pad) GT[(long long)(v0 + j) * ep.c_pad + n] = (T)acc[bi][bj][4 * i + j];
         }
-        *reinterpret_cast<uint4*>(GT + (long long)v * ep.c_pad + n0) =
-            *reinterpret_cast<const uint4*>(tmp);
       }
+    }
+  // --- G[n][v]: each wavefront stages its 32-token x 128-row blocks (rounded
+  // to T) in its own LDS rows and stores whole 128-value rows.
+  constexpr int kPitch = 128 * (int)sizeof(T) + 16;    // bytes per staged token row
+  constexpr int kChunks = 128 * (int)sizeof(T) / 16;   // 16-byte chunks per row
+  constexpr int EPC = 16 / sizeof(T);
+  static_assert(8 * 32 * kPitch <= Smem<BN>::kBytes, "per-wavefront G staging");
+  char* const reg = lds + wave * 32 * kPitch;
+#pragma unroll
+  for (int bj = 0; bj < NBJ; ++bj) {
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        T v4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v4[j] = (T)acc[bi][bj][4 * i + j];
+        char* dst = reg + r32 * kPitch + (bi * 32 + 8 * i + 4 * h) * (int)sizeof(T);
+        if constexpr (sizeof(T) == 2)
+          *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(v4);
+        else
+          *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(v4);
+      }
+#pragma unroll
+    for (int it = 0; it < 32 * kChunks / 64; ++it) {
+      const int q = it * 64 + lane;
+      const int row = q / kChunks, c = q % kChunks;
+      const uint4 val = *reinterpret_cast<const uint4*>(reg + row * kPitch + c * 16);
+      const int n = n_wave + bj * 32 + row;
+      const int v = v_wave + c * EPC;
+      if (n < ep.c_pad && v < ep.v_pad) *reinterpret_cast<uint4*>(G + (long long)n * ep.v_pad + v) = val;
     }
   }
 }

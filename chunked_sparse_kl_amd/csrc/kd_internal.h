@@ -28,6 +28,15 @@ struct Ctrl {
 
 enum class DType { BF16 = 0, F32 = 1 };
 
+// One unmasked teacher entry (row, k), bucketed by (vocabulary tile, 64-row
+// block): its row, k, vocabulary id and renormalised probability p_{row,k}.
+struct alignas(16) Hit {
+  int row;
+  int k;
+  int v;
+  float p;
+};
+
 inline size_t elem_size(DType t) { return t == DType::BF16 ? 2 : 4; }
 // K elements per GEMM main-loop block; KPAD is a multiple of it for both types.
 inline int k_block(DType t) { return KBLOCK_BYTES / (int)elem_size(t); }
@@ -39,8 +48,8 @@ void launch_teacher_prep(const float* logp, const int* idx, const uint8_t* mask,
                          float* p, float* S, float* E, int* counts, int n_rb, Ctrl* ctrl,
                          hipStream_t s);
 void launch_scan(const int* counts, int n_keys, int* offsets, int* cursor, int* tmp, hipStream_t s);
-void launch_hit_scatter(const int* idx, const uint8_t* mask, int n, int K, int V, int n_rb,
-                        int* cursor, int2* hits, hipStream_t s);
+void launch_hit_scatter(const int* idx, const float* p, const uint8_t* mask, int n, int K, int V,
+                        int n_rb, int* cursor, Hit* hits, hipStream_t s);
 void launch_lse_kl(const float2* part, int ld_part, int n_vt, int c0, int rows, const float* p,
                    const float* g, const float* S, const float* E, const uint8_t* mask, int K,
                    float* lse, float* row_kl, hipStream_t s);
@@ -61,8 +70,7 @@ struct FwdEpilogue {
   int K;
   int n_rb;
   const int* hit_off;  // [n_vt * n_rb + 1]
-  const int2* hits;    // (row, k) sorted by (vocab tile, row block)
-  const int* idx;      // [n, K]
+  const Hit* hits;     // bucketed by (vocab tile, row block)
   float* g;            // [n, K] gathered logits
 };
 
@@ -77,9 +85,7 @@ struct RecomputeEpilogue {
   int K;
   int n_rb;
   const int* hit_off;
-  const int2* hits;
-  const int* idx;
-  const float* p;      // [n, K] renormalised teacher probabilities
+  const Hit* hits;
   const float* S;      // [n]
   const float* lse;    // [n]
   const uint8_t* mask; // [n] or null

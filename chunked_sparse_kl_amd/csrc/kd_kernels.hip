@@ -185,10 +185,11 @@ __global__ __launch_bounds__(kScanThreads) void scan_apply_kernel(const int* __r
 // One wavefront per row: places every (row, k) of an unmasked row with a valid
 // id into its (vocabulary tile, row block) bucket.
 __global__ __launch_bounds__(256) void hit_scatter_kernel(const int* __restrict__ idx,
+                                                          const float* __restrict__ p,
                                                           const uint8_t* __restrict__ mask, int n,
                                                           int K, int V, int n_rb,
                                                           int* __restrict__ cursor,
-                                                          int2* __restrict__ hits) {
+                                                          Hit* __restrict__ hits) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= n) return;
@@ -199,7 +200,12 @@ __global__ __launch_bounds__(256) void hit_scatter_kernel(const int* __restrict_
     const int v = idx[base + k];
     if (v >= 0 && v < V) {
       const int pos = atomicAdd(&cursor[(v / TILE_V) * n_rb + rb], 1);
-      hits[pos] = make_int2(row, k);
+      Hit h;
+      h.row = row;
+      h.k = k;
+      h.v = v;
+      h.p = p[base + k];
+      hits[pos] = h;
     }
   }
 }
@@ -344,9 +350,9 @@ void launch_scan(const int* counts, int n_keys, int* offsets, int* cursor, int* 
   scan_apply_kernel<<<tiles, kScanThreads, 0, s>>>(counts, n_keys, tmp, offsets, cursor);
 }
 
-void launch_hit_scatter(const int* idx, const uint8_t* mask, int n, int K, int V, int n_rb,
-                        int* cursor, int2* hits, hipStream_t s) {
-  hit_scatter_kernel<<<(n + 3) / 4, 256, 0, s>>>(idx, mask, n, K, V, n_rb, cursor, hits);
+void launch_hit_scatter(const int* idx, const float* p, const uint8_t* mask, int n, int K, int V,
+                        int n_rb, int* cursor, Hit* hits, hipStream_t s) {
+  hit_scatter_kernel<<<(n + 3) / 4, 256, 0, s>>>(idx, p, mask, n, K, V, n_rb, cursor, hits);
 }
 
 void launch_lse_kl(const float2* part, int ld_part, int n_vt, int c0, int rows, const float* p,
