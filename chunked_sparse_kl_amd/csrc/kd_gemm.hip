@@ -738,14 +738,11 @@ constexpr int kPlainWC = KD_PLAIN_WC;          // wavefront columns of the dH / 
 constexpr int kPlainThreads = 128 * kPlainWC;
 
 template <typename T, bool kAccumulate>
-__global__ __launch_bounds__(kPlainThreads, 1) void plain_gemm_kernel(Operand A, Operand B, int k_elems,
-                                                                       int tiles_m, int tiles_n,
-                                                                       int splits, int kb_per_split,
-                                                                       float* out, long long ld_out,
-                                                                       long long split_stride, int M,
-                                                                       int N) {
+__device__ inline void plain_gemm(char* lds, Operand A, Operand B, int k_elems, int tiles_m,
+                                  int tiles_n, int splits, int kb_per_split, float* out,
+                                  long long ld_out, long long split_stride, int M, int N) {
   constexpr int BN = TILE_D, WC = kPlainWC, NBJ = BN / (32 * WC);
-  KD_DECLARE_LDS(BN);
+  
   const TileIdx ti = map_tile<8>(tiles_m, tiles_n, splits);
   const int kb_total = (k_elems + Traits<T>::BK - 1) / Traits<T>::BK;
   const int kb0 = ti.split * kb_per_split;
@@ -785,6 +782,28 @@ __global__ __launch_bounds__(kPlainThreads, 1) void plain_gemm_kernel(Operand A,
         }
       }
     }
+}
+
+// Distinct kernel names for dH (split-K partials, plain stores) and dW
+// (accumulated into the caller's fp32 dW).
+template <typename T>
+__global__ __launch_bounds__(kPlainThreads, 1) void dh_gemm_kernel(Operand A, Operand B, int k_elems,
+                                                                    int tiles_m, int tiles_n, int splits,
+                                                                    int kb_per_split, float* out,
+                                                                    long long ld_out,
+                                                                    long long split_stride, int M, int N) {
+  KD_DECLARE_LDS(TILE_D);
+  plain_gemm<T, false>(lds, A, B, k_elems, tiles_m, tiles_n, splits, kb_per_split, out, ld_out,
+                       split_stride, M, N);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kPlainThreads, 1) void dw_gemm_kernel(Operand A, Operand B, int k_elems,
+                                                                    int tiles_m, int tiles_n,
+                                                                    int kb_per_split, float* out,
+                                                                    long long ld_out, int M, int N) {
+  KD_DECLARE_LDS(TILE_D);
+  plain_gemm<T, true>(lds, A, B, k_elems, tiles_m, tiles_n, 1, kb_per_split, out, ld_out, 0, M, N);
 }
 
 template <typename T>
@@ -838,11 +857,11 @@ void launch_dh_gemm(DType t, const void* G, int rows, int v_pad, const void* WT,
   const int kb_per = (kb_total + splits - 1) / splits;
   const int grid = tiles_m * tiles_n * splits;
   if (t == DType::BF16)
-    plain_gemm_kernel<__bf16, false><<<grid, kPlainThreads, 0, s>>>(
+    dh_gemm_kernel<__bf16><<<grid, kPlainThreads, 0, s>>>(
         make_operand<__bf16>(G, v_pad, rows), make_operand<__bf16>(WT, v_pad, d), v_pad, tiles_m,
         tiles_n, splits, kb_per, part, d, split_stride, rows, d);
   else
-    plain_gemm_kernel<float, false><<<grid, kPlainThreads, 0, s>>>(
+    dh_gemm_kernel<float><<<grid, kPlainThreads, 0, s>>>(
         make_operand<float>(G, v_pad, rows), make_operand<float>(WT, v_pad, d), v_pad, tiles_m,
         tiles_n, splits, kb_per, part, d, split_stride, rows, d);
 }
@@ -854,13 +873,13 @@ void launch_dw_gemm(DType t, const void* GT, int V, int c_pad, const void* HT, i
   const int kb_total = (c_pad + bk - 1) / bk;
   const int grid = tiles_m * tiles_n;
   if (t == DType::BF16)
-    plain_gemm_kernel<__bf16, true><<<grid, kPlainThreads, 0, s>>>(
+    dw_gemm_kernel<__bf16><<<grid, kPlainThreads, 0, s>>>(
         make_operand<__bf16>(GT, c_pad, V), make_operand<__bf16>(HT, c_pad, d), c_pad, tiles_m,
-        tiles_n, 1, kb_total, dW, d, 0, V, d);
+        tiles_n, kb_total, dW, d, V, d);
   else
-    plain_gemm_kernel<float, true><<<grid, kPlainThreads, 0, s>>>(
+    dw_gemm_kernel<float><<<grid, kPlainThreads, 0, s>>>(
         make_operand<float>(GT, c_pad, V), make_operand<float>(HT, c_pad, d), c_pad, tiles_m,
-        tiles_n, 1, kb_total, dW, d, 0, V, d);
+        tiles_n, kb_total, dW, d, V, d);
 }
 
 }  // namespace kd
