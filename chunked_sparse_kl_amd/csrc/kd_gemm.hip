@@ -742,7 +742,6 @@ __device__ inline void plain_gemm(char* lds, Operand A, Operand B, int k_elems, 
                                   int tiles_n, int splits, int kb_per_split, float* out,
                                   long long ld_out, long long split_stride, int M, int N) {
   constexpr int BN = TILE_D, WC = kPlainWC, NBJ = BN / (32 * WC);
-  
   const TileIdx ti = map_tile<8>(tiles_m, tiles_n, splits);
   const int kb_total = (k_elems + Traits<T>::BK - 1) / Traits<T>::BK;
   const int kb0 = ti.split * kb_per_split;
@@ -753,35 +752,56 @@ __device__ inline void plain_gemm(char* lds, Operand A, Operand B, int k_elems, 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave / WC, wc = wave % WC, r32 = lane & 31, h = lane >> 5;
   float* o = out + ti.split * split_stride;
-  // One 32x32 block at a time: for accumulation, all 16 old values are loaded
-  // before any store so the loads are issued back to back.
+  constexpr int NB = 4 * NBJ;  // 32x32 blocks of this wavefront, b = bi * NBJ + bj
+  auto row0 = [&](int b) { return ti.tm * BM + wr * 128 + (b / NBJ) * 32 + 4 * h; };
+  auto col = [&](int b) { return ti.tn * BN + wc * (BN / WC) + (b % NBJ) * 32 + r32; };
+  if (kAccumulate) {
+    // out += D.  The old values of block b + kAhead are loaded before block b
+    // is stored (in program order, since loads and stores may alias), so
+    // their latency overlaps; the K loop's fragment registers are free now.
+    // Buffer accesses over this tile's valid rows with an out-of-range offset
+    // for elements outside the output keep the code free of branches (so the
+    // compiler can count outstanding loads precisely).
+    constexpr int kAhead = 3;
+    const int m_tile = ti.tm * BM;
+    const int rows_ok = min(M - m_tile, BM);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        o + (long long)m_tile * ld_out, (short)0, (int)(rows_ok * ld_out * 4), 0x00020000);
+    // Rows past the output end fall outside num_records by themselves; a
+    // column past N gets bit 31 added (arithmetic, not a select, which the
+    // compiler would turn back into branches).
+    auto off = [&](int b, int e) -> unsigned {
+      const int n = col(b), m = row0(b) + 8 * (e >> 2) + (e & 3);
+      const unsigned past = (unsigned)(N - 1 - n) >> 31;
+      return (unsigned)(((m - m_tile) * ld_out + n) * 4) + (past << 31);
+    };
+    float old[NB][16];
+    auto load = [&](int b) {
 #pragma unroll
-  for (int bi = 0; bi < 4; ++bi)
+      for (int e = 0; e < 16; ++e)
+        old[b][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off(b, e), 0, 0));
+    };
 #pragma unroll
-    for (int bj = 0; bj < NBJ; ++bj) {
-      const int n = ti.tn * BN + wc * (BN / WC) + bj * 32 + r32;
-      const int m0 = ti.tm * BM + wr * 128 + bi * 32 + 4 * h;
-      const bool n_ok = n < N;
-      if (kAccumulate) {
-        float old[16];
+    for (int b = 0; b < kAhead; ++b) load(b);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int m = m0 + 8 * (e >> 2) + (e & 3);
-          old[e] = (n_ok && m < M) ? __builtin_nontemporal_load(o + (long long)m * ld_out + n) : 0.f;
-        }
+    for (int b = 0; b < NB; ++b) {
+      if (b + kAhead < NB) load(b + kAhead);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int m = m0 + 8 * (e >> 2) + (e & 3);
-          if (n_ok && m < M) o[(long long)m * ld_out + n] = old[e] + acc[bi][bj][e];
-        }
-      } else {
+      for (int e = 0; e < 16; ++e)
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, old[b][e] + acc[b / NBJ][b % NBJ][e]), rs,
+                                              off(b, e), 0, 0);
+    }
+  } else {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int m = m0 + 8 * (e >> 2) + (e & 3);
-          if (n_ok && m < M) o[(long long)m * ld_out + n] = acc[bi][bj][e];
-        }
+    for (int b = 0; b < NB; ++b) {
+      const int n = col(b), m0 = row0(b);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + 8 * (e >> 2) + (e & 3);
+        if (n < N && m < M) o[(long long)m * ld_out + n] = acc[b / NBJ][b % NBJ][e];
       }
     }
+  }
 }
 
 // Distinct kernel names for dH (split-K partials, plain stores) and dW
