@@ -123,16 +123,15 @@ int check_launch(const char* what) {
 constexpr size_t kAlign = 256;
 constexpr int64_t kMaxAutoChunk = 8192;
 constexpr size_t kWorkspaceCap = size_t(24) << 30;
-constexpr int kScanTile = 4096;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 struct Layout {
   DType dt;
-  int64_t n, d, V, K, chunk, c_pad, v_pad, n_vt, n_rb, n_keys, splits, scan_tiles;
+  int64_t n, d, V, K, chunk, c_pad, v_pad, n_vt, n_rb, splits;
   // byte offsets
-  size_t ctrl, p, S, E, counts, offs, cursor, scan_tmp, hits, common_end;
+  size_t ctrl, p, S, E, hit_off, hits, common_end;
   size_t part, g, rowkl, fwd_end;
   size_t G, GT, WT, HT, dhpart, bwd_end;
 };
@@ -175,9 +174,7 @@ Layout make_layout(DType dt, int64_t n, int64_t d, int64_t V, int64_t K, int64_t
   L.v_pad = round_up(V, kd::KPAD);
   L.n_vt = (V + kd::TILE_V - 1) / kd::TILE_V;
   L.n_rb = (n + kd::ROW_BLOCK - 1) / kd::ROW_BLOCK;
-  L.n_keys = L.n_vt * L.n_rb;
   L.splits = dh_splits(dt, L.c_pad, d, L.v_pad);
-  L.scan_tiles = (L.n_keys + kScanTile - 1) / kScanTile;
   const size_t es = kd::elem_size(dt);
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -189,11 +186,8 @@ Layout make_layout(DType dt, int64_t n, int64_t d, int64_t V, int64_t K, int64_t
   L.p = take(size_t(n) * K * 4);
   L.S = take(size_t(n) * 4);
   L.E = take(size_t(n) * 4);
-  L.counts = take(size_t(L.n_keys) * 4);
-  L.offs = take(size_t(L.n_keys + 1) * 4);
-  L.cursor = take(size_t(L.n_keys) * 4);
-  L.scan_tmp = take(size_t(L.scan_tiles + 1) * 4);
-  L.hits = take(size_t(n) * K * sizeof(kd::Hit));
+  L.hit_off = take(size_t(L.n_rb) * (L.n_vt + 1) * 4);
+  L.hits = take(size_t(L.n_rb) * kd::ROW_BLOCK * K * sizeof(kd::Hit));
   L.common_end = o;
   // forward-only region
   L.part = take(size_t(L.n_vt) * chunk * 8);
@@ -221,11 +215,11 @@ int check_sizes(int dtype, int64_t n, int64_t d, int64_t V, int64_t K) {
   if (d % epc != 0)
     return fail(KD_E_INVAL, "d=%lld must be a multiple of %lld (16-byte rows)", (long long)d, (long long)epc);
   const int64_t lim = (int64_t(1) << 31) - 1;
-  if (n > lim || V > lim - 4096 || d > lim || n * K > lim)
+  if (n > lim || V > lim - 4096 || d > lim || (n + kd::ROW_BLOCK) * K > lim)
     return fail(KD_E_INVAL, "sizes exceed the 32-bit index range of the kernels");
-  const int64_t n_keys = ((V + 255) / 256) * ((n + 63) / 64);
-  if ((n_keys + kScanTile - 1) / kScanTile > kScanTile)
-    return fail(KD_E_INVAL, "too many teacher-hit buckets (%lld)", (long long)n_keys);
+  if ((V + kd::TILE_V - 1) / kd::TILE_V > kd::kMaxVocabTiles)
+    return fail(KD_E_INVAL, "V=%lld exceeds the supported vocabulary of %lld", (long long)V,
+                (long long)kd::kMaxVocabTiles * kd::TILE_V);
   return KD_OK;
 }
 
@@ -306,15 +300,15 @@ int check_common(const void* H, const void* W, const int32_t* idx, const float* 
 int prepare_teacher(const Layout& L, const int32_t* idx, const float* logp, const uint8_t* mask,
                     char* ws, hipStream_t s) {
   auto* ctrl = reinterpret_cast<kd::Ctrl*>(ws + L.ctrl);
-  int* counts = reinterpret_cast<int*>(ws + L.counts);
   const int n = (int)L.n, K = (int)L.K, V = (int)L.V;
   const double nk = double(L.n) * L.K;
   KD_LAUNCH("fill", 0, 0, kd::launch_fill_i32(reinterpret_cast<int*>(ctrl), 64, 0, s));
-  KD_LAUNCH("fill", 0, 0, kd::launch_fill_i32(counts, L.n_keys, 0, s));
-  KD_LAUNCH("teacher_prep", 0, nk * 12 + L.n * 9.0,
-            kd::launch_teacher_prep(logp, idx, mask, n, K, V, reinterpret_cast<float*>(ws + L.p),
-                                    reinterpret_cast<float*>(ws + L.S),
-                                    reinterpret_cast<float*>(ws + L.E), counts, (int)L.n_rb, ctrl, s));
+  KD_LAUNCH("teacher_bucket", 0, nk * 32 + L.n * 9.0,
+            kd::launch_teacher_bucket(logp, idx, mask, n, K, V, reinterpret_cast<float*>(ws + L.p),
+                                      reinterpret_cast<float*>(ws + L.S),
+                                      reinterpret_cast<float*>(ws + L.E),
+                                      reinterpret_cast<int*>(ws + L.hit_off),
+                                      reinterpret_cast<kd::Hit*>(ws + L.hits), ctrl, s));
   if (g_validate.load()) {
     kd::Ctrl host{};
     hipError_t e = hipMemcpyAsync(&host, ctrl, sizeof(int) * 2, hipMemcpyDeviceToHost, s);
@@ -323,14 +317,6 @@ int prepare_teacher(const Layout& L, const int32_t* idx, const float* logp, cons
     if (host.range_error)
       return fail(KD_E_RANGE, "an unmasked row holds a teacher id outside [0, %d)", V);
   }
-  KD_LAUNCH("hit_scan", 0, L.n_keys * 12.0,
-            kd::launch_scan(counts, (int)L.n_keys, reinterpret_cast<int*>(ws + L.offs),
-                            reinterpret_cast<int*>(ws + L.cursor),
-                            reinterpret_cast<int*>(ws + L.scan_tmp), s));
-  KD_LAUNCH("hit_scatter", 0, nk * 12,
-            kd::launch_hit_scatter(idx, reinterpret_cast<const float*>(ws + L.p), mask, n, K, V,
-                                   (int)L.n_rb, reinterpret_cast<int*>(ws + L.cursor),
-                                   reinterpret_cast<kd::Hit*>(ws + L.hits), s));
   return KD_OK;
 }
 
@@ -432,8 +418,8 @@ int kd_fused_chunked_kl_fwd(int dtype, const void* H, const void* W, const int32
     ep.rows = rows;
     ep.V = (int)L.V;
     ep.K = (int)L.K;
-    ep.n_rb = (int)L.n_rb;
-    ep.hit_off = reinterpret_cast<const int*>(ws + L.offs);
+    ep.hit_ld = (int)L.n_vt + 1;
+    ep.hit_off = reinterpret_cast<const int*>(ws + L.hit_off);
     ep.hits = reinterpret_cast<const kd::Hit*>(ws + L.hits);
     ep.g = g;
     const char* Hc = static_cast<const char*>(H) + c0 * L.d * es;
@@ -488,8 +474,8 @@ int kd_fused_chunked_kl_bwd(int dtype, const void* H, const void* W, const int32
     ep.rows = rows;
     ep.V = (int)L.V;
     ep.K = (int)L.K;
-    ep.n_rb = (int)L.n_rb;
-    ep.hit_off = reinterpret_cast<const int*>(ws + L.offs);
+    ep.hit_ld = (int)L.n_vt + 1;
+    ep.hit_off = reinterpret_cast<const int*>(ws + L.hit_off);
     ep.hits = reinterpret_cast<const kd::Hit*>(ws + L.hits);
     ep.S = reinterpret_cast<const float*>(ws + L.S);
     ep.lse = lse;

@@ -477,8 +477,8 @@ __device__ inline void acc_add(f32x16 (&acc)[4][kFusedNBJ], int q, float x) {
 #undef KD_GET
 #undef KD_ADD
 
-// The teacher entries of one wavefront: the bucket of (vocabulary tile tm,
-// the 64-row block of its tokens).  The first 64 entries (one per lane) are
+// The teacher entries of one wavefront: the bucket of (the 64-row block of its
+// tokens, vocabulary tile tm).  The first 64 entries (one per lane) are
 // loaded before the K loop so their latency hides under it.
 struct WaveHits {
   int lo, hi;      // bucket range in the hit array
@@ -486,14 +486,14 @@ struct WaveHits {
   int v_lo;        // first vocabulary id of the wavefront's 128 rows
   Hit pre;         // this lane's entry among the first 64
 
-  __device__ inline void init(const int* hit_off, const Hit* hits, int n_rb, int tm, int c0, int rows,
+  __device__ inline void init(const int* hit_off, const Hit* hits, int hit_ld, int tm, int c0, int rows,
                               int tok0, int v_lo_) {
     const int lane = threadIdx.x & 63;
     row0 = c0 + tok0;
     v_lo = v_lo_;
     lo = hi = 0;
     if (tok0 < rows) {  // tokens past the chunk end have no bucket
-      const int key = tm * n_rb + row0 / ROW_BLOCK;
+      const int key = (row0 / ROW_BLOCK) * hit_ld + tm;
       lo = hit_off[key];
       hi = hit_off[key + 1];
     }
@@ -547,7 +547,7 @@ __global__ __launch_bounds__(kFusedThreads, 1) void fwd_gemm_kernel(Operand A, O
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = wave / WC, wc = wave % WC, r32 = lane & 31, h = lane >> 5;
   WaveHits wh;
-  wh.init(ep.hit_off, ep.hits, ep.n_rb, ti.tm, ep.c0, ep.rows, ti.tn * BN + wc * 64,
+  wh.init(ep.hit_off, ep.hits, ep.hit_ld, ti.tm, ep.c0, ep.rows, ti.tn * BN + wc * 64,
           ti.tm * BM + wr * 128);
   f32x16 acc[4][NBJ];
   const int kb_end = (k_elems + Traits<T>::BK - 1) / Traits<T>::BK;
@@ -632,7 +632,7 @@ __global__ __launch_bounds__(kFusedThreads, 1) void recompute_gemm_kernel(Operan
   const int n_wave = ti.tn * BN + wc * 64;  // chunk-local first token of this wavefront
   const int v_wave = ti.tm * BM + wr * 128; // first vocabulary row of this wavefront
   WaveHits wh;
-  wh.init(ep.hit_off, ep.hits, ep.n_rb, ti.tm, ep.c0, ep.rows, n_wave, v_wave);
+  wh.init(ep.hit_off, ep.hits, ep.hit_ld, ti.tm, ep.c0, ep.rows, n_wave, v_wave);
   f32x16 acc[4][NBJ];
   const int kb_end = (k_elems + Traits<T>::BK - 1) / Traits<T>::BK;
   gemm_mainloop<T, BN, WC>(A, B, k_elems, ti.tm, ti.tn, 0, kb_end, lds, acc);

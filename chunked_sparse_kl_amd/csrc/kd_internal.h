@@ -44,12 +44,14 @@ static_assert(KPAD % (KBLOCK_BYTES / 2) == 0, "dH / dW contractions must hold wh
 
 // ---------------------------------------------------------------- small kernels
 void launch_fill_i32(int* p, long long count, int value, hipStream_t s);
-void launch_teacher_prep(const float* logp, const int* idx, const uint8_t* mask, int n, int K, int V,
-                         float* p, float* S, float* E, int* counts, int n_rb, Ctrl* ctrl,
-                         hipStream_t s);
-void launch_scan(const int* counts, int n_keys, int* offsets, int* cursor, int* tmp, hipStream_t s);
-void launch_hit_scatter(const int* idx, const float* p, const uint8_t* mask, int n, int K, int V,
-                        int n_rb, int* cursor, Hit* hits, hipStream_t s);
+// Teacher preparation and bucketing, one workgroup per 64-row block.  Bucket
+// (row block rb, vocabulary tile j) holds the unmasked entries of rb whose id
+// lies in tile j, at hits[hit_off[rb * (n_vt + 1) + j] .. hit_off[... + j + 1]);
+// row block rb owns the hit range [rb * 64 * K, (rb + 1) * 64 * K).
+constexpr int kMaxVocabTiles = 16383;  // LDS bucket counters of one workgroup (64 KB)
+void launch_teacher_bucket(const float* logp, const int* idx, const uint8_t* mask, int n, int K,
+                           int V, float* p, float* S, float* E, int* hit_off, Hit* hits,
+                           Ctrl* ctrl, hipStream_t s);
 void launch_lse_kl(const float2* part, int ld_part, int n_vt, int c0, int rows, const float* p,
                    const float* g, const float* S, const float* E, const uint8_t* mask, int K,
                    float* lse, float* row_kl, hipStream_t s);
@@ -68,9 +70,9 @@ struct FwdEpilogue {
   int rows;            // rows in this chunk
   int V;
   int K;
-  int n_rb;
-  const int* hit_off;  // [n_vt * n_rb + 1]
-  const Hit* hits;     // bucketed by (vocab tile, row block)
+  int hit_ld;          // n_vt + 1: bucket offsets per row block
+  const int* hit_off;  // [n_rb][n_vt + 1]
+  const Hit* hits;     // bucketed by (row block, vocab tile)
   float* g;            // [n, K] gathered logits
 };
 
@@ -83,7 +85,7 @@ struct RecomputeEpilogue {
   int rows;
   int V;
   int K;
-  int n_rb;
+  int hit_ld;
   const int* hit_off;
   const Hit* hits;
   const float* S;      // [n]

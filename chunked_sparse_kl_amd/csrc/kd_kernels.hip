@@ -37,182 +37,132 @@ __global__ void fill_i32_kernel(int* p, long long count, int value) {
   for (; i < count; i += stride) p[i] = value;
 }
 
-// One wavefront per row.  Renormalises the teacher's K log-values (the offline
-// top-K cache of the blog's "Two systems changes"), stores p = exp(l), S = sum p,
-// E = sum p*l (0*log 0 := 0), counts unmasked rows and histograms the teacher
-// ids by (vocabulary tile, row block).  Masked rows are skipped entirely.
-__global__ __launch_bounds__(256) void teacher_prep_kernel(
-    const float* __restrict__ logp, const int* __restrict__ idx, const uint8_t* __restrict__ mask,
-    int n, int K, int V, float* __restrict__ p, float* __restrict__ S, float* __restrict__ E,
-    int* __restrict__ counts, int n_rb, Ctrl* ctrl) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= n) return;
-  const long long base = (long long)row * K;
-  const bool live = mask == nullptr || mask[row] != 0;
-  if (!live) {
-    for (int k = lane; k < K; k += 64) p[base + k] = 0.f;
-    if (lane == 0) {
-      S[row] = 0.f;
-      E[row] = 0.f;
-    }
-    return;
-  }
-  float mx = kNegInf;
-  for (int k = lane; k < K; k += 64) mx = fmaxf(mx, logp[base + k]);
-  mx = wave_max(mx);
-  float se = 0.f;
-  for (int k = lane; k < K; k += 64) se += expf(logp[base + k] - mx);
-  se = wave_sum(se);
-  const float lam = mx + logf(se);
-  float s = 0.f, e = 0.f;
-  for (int k = lane; k < K; k += 64) {
-    const float l = logp[base + k] - lam;
-    const float pk = expf(l);
-    p[base + k] = pk;
-    s += pk;
-    e += pk > 0.f ? pk * l : 0.f;
-  }
-  s = wave_sum(s);
-  e = wave_sum(e);
-  if (lane == 0) {
-    S[row] = s;
-    E[row] = e;
-    atomicAdd(&ctrl->n_valid, 1);
-  }
-  const int rb = row / ROW_BLOCK;
-  bool bad = false;
-  for (int k = lane; k < K; k += 64) {
-    const int v = idx[base + k];
-    if (v >= 0 && v < V)
-      atomicAdd(&counts[(v / TILE_V) * n_rb + rb], 1);
-    else
-      bad = true;
-  }
-  if (__any(bad) && lane == 0) ctrl->range_error = 1;
-}
-
-// Block-level exclusive scan of 4096 ints (1024 threads x 4), deterministic.
-constexpr int kScanThreads = 1024;
-constexpr int kScanItems = 4;
-constexpr int kScanTile = kScanThreads * kScanItems;
-
-__device__ inline int block_exclusive_scan(int v, int* sh_waves, int* total) {
+// Exclusive scan over the 256 threads of a workgroup (fixed order); *total
+// receives the sum.  sh: 4 ints of LDS.
+__device__ inline int block256_exclusive_scan(int v, int* sh, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int incl = v;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    int t = __shfl_up(incl, o, 64);
+    const int t = __shfl_up(incl, o, 64);
     if (lane >= o) incl += t;
   }
-  if (lane == 63) sh_waves[wave] = incl;
+  if (lane == 63) sh[wave] = incl;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int w = 0; w < kScanThreads / 64; ++w) {
-      int t = sh_waves[w];
-      sh_waves[w] = acc;
-      acc += t;
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += sh[w];
+  *total = sh[0] + sh[1] + sh[2] + sh[3];
+  __syncthreads();
+  return base + incl - v;
+}
+
+// One workgroup (4 wavefronts) per 64-row block.  Each wavefront takes one row
+// at a time: renormalises the teacher's K log-values (the offline top-K cache
+// of the blog's "Two systems changes"), stores p = exp(l), S = sum p and
+// E = sum p*l (0*log 0 := 0), and counts the row's ids per vocabulary tile in
+// LDS.  The counts are then scanned into this block's bucket offsets and every
+// entry is placed in its bucket with LDS cursors.  Masked rows are skipped
+// entirely; ids outside [0, V) set the range flag and are dropped.
+__global__ __launch_bounds__(256) void teacher_bucket_kernel(
+    const float* __restrict__ logp, const int* __restrict__ idx, const uint8_t* __restrict__ mask,
+    int n, int K, int V, int n_vt, float* __restrict__ p, float* __restrict__ S,
+    float* __restrict__ E, int* __restrict__ hit_off, Hit* __restrict__ hits, Ctrl* ctrl) {
+  extern __shared__ int cnt[];  // n_vt + 1 counters, then cursors
+  __shared__ int sh[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rb = blockIdx.x;
+  const int row_lo = rb * ROW_BLOCK, row_hi = min(row_lo + ROW_BLOCK, n);
+  const int n_ct = n_vt + 1;
+  for (int j = tid; j < n_ct; j += 256) cnt[j] = 0;
+  __syncthreads();
+
+  int live_rows = 0;
+  bool bad = false;
+  for (int row = row_lo + wave; row < row_hi; row += 4) {
+    const long long base = (long long)row * K;
+    if (mask != nullptr && mask[row] == 0) {
+      for (int k = lane; k < K; k += 64) p[base + k] = 0.f;
+      if (lane == 0) {
+        S[row] = 0.f;
+        E[row] = 0.f;
+      }
+      continue;
     }
-    *total = acc;
-  }
-  __syncthreads();
-  int r = sh_waves[wave] + incl - v;
-  __syncthreads();
-  return r;
-}
-
-__global__ __launch_bounds__(kScanThreads) void scan_tiles_kernel(const int* __restrict__ in, int n,
-                                                                   int* __restrict__ tile_tot) {
-  __shared__ int sh[kScanThreads / 64];
-  __shared__ int tot;
-  const long long b = (long long)blockIdx.x * kScanTile + threadIdx.x * kScanItems;
-  int s = 0;
-#pragma unroll
-  for (int i = 0; i < kScanItems; ++i) s += (b + i < n) ? in[b + i] : 0;
-  block_exclusive_scan(s, sh, &tot);
-  if (threadIdx.x == 0) tile_tot[blockIdx.x] = tot;
-}
-
-__global__ __launch_bounds__(kScanThreads) void scan_totals_kernel(int* tile_tot, int n_tiles) {
-  // exclusive scan in place of up to kScanTile tile totals (single block)
-  __shared__ int sh[kScanThreads / 64];
-  __shared__ int tot;
-  int vals[kScanItems];
-  int s = 0;
-#pragma unroll
-  for (int i = 0; i < kScanItems; ++i) {
-    const int j = threadIdx.x * kScanItems + i;
-    vals[i] = j < n_tiles ? tile_tot[j] : 0;
-    s += vals[i];
-  }
-  int run = block_exclusive_scan(s, sh, &tot);
-#pragma unroll
-  for (int i = 0; i < kScanItems; ++i) {
-    const int j = threadIdx.x * kScanItems + i;
-    if (j < n_tiles) tile_tot[j] = run;
-    run += vals[i];
-  }
-  if (threadIdx.x == 0) tile_tot[n_tiles] = tot;
-}
-
-__global__ __launch_bounds__(kScanThreads) void scan_apply_kernel(const int* __restrict__ in, int n,
-                                                                  const int* __restrict__ tile_tot,
-                                                                  int* __restrict__ out,
-                                                                  int* __restrict__ cursor) {
-  __shared__ int sh[kScanThreads / 64];
-  __shared__ int tot;
-  const long long b = (long long)blockIdx.x * kScanTile + threadIdx.x * kScanItems;
-  int vals[kScanItems];
-  int s = 0;
-#pragma unroll
-  for (int i = 0; i < kScanItems; ++i) {
-    vals[i] = (b + i < n) ? in[b + i] : 0;
-    s += vals[i];
-  }
-  int run = block_exclusive_scan(s, sh, &tot) + tile_tot[blockIdx.x];
-#pragma unroll
-  for (int i = 0; i < kScanItems; ++i) {
-    if (b + i < n) {
-      out[b + i] = run;
-      cursor[b + i] = run;
+    ++live_rows;
+    float mx = kNegInf;
+    for (int k = lane; k < K; k += 64) mx = fmaxf(mx, logp[base + k]);
+    mx = wave_max(mx);
+    float se = 0.f;
+    for (int k = lane; k < K; k += 64) se += expf(logp[base + k] - mx);
+    se = wave_sum(se);
+    const float lam = mx + logf(se);
+    float sp = 0.f, e = 0.f;
+    for (int k = lane; k < K; k += 64) {
+      const float l = logp[base + k] - lam;
+      const float pk = expf(l);
+      p[base + k] = pk;
+      sp += pk;
+      e += pk > 0.f ? pk * l : 0.f;
+      const int v = idx[base + k];
+      if (v >= 0 && v < V)
+        atomicAdd(&cnt[v / TILE_V], 1);
+      else
+        bad = true;
     }
-    run += vals[i];
-  }
-  if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) out[n] = tile_tot[gridDim.x];
-}
-
-// One wavefront per row: places every (row, k) of an unmasked row with a valid
-// id into its (vocabulary tile, row block) bucket.
-__global__ __launch_bounds__(256) void hit_scatter_kernel(const int* __restrict__ idx,
-                                                          const float* __restrict__ p,
-                                                          const uint8_t* __restrict__ mask, int n,
-                                                          int K, int V, int n_rb,
-                                                          int* __restrict__ cursor,
-                                                          Hit* __restrict__ hits) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= n) return;
-  if (mask != nullptr && mask[row] == 0) return;
-  const long long base = (long long)row * K;
-  const int rb = row / ROW_BLOCK;
-  for (int k = lane; k < K; k += 64) {
-    const int v = idx[base + k];
-    if (v >= 0 && v < V) {
-      const int pos = atomicAdd(&cursor[(v / TILE_V) * n_rb + rb], 1);
-      Hit h;
-      h.row = row;
-      h.k = k;
-      h.v = v;
-      h.p = p[base + k];
-      hits[pos] = h;
+    sp = wave_sum(sp);
+    e = wave_sum(e);
+    if (lane == 0) {
+      S[row] = sp;
+      E[row] = e;
     }
   }
+  if (lane == 0 && live_rows > 0) atomicAdd(&ctrl->n_valid, live_rows);
+  if (__any(bad) && lane == 0) ctrl->range_error = 1;
+  __syncthreads();
+
+  // Exclusive scan of the n_vt + 1 counters (the last one is 0, so it ends as
+  // the block's total); thread t owns a contiguous run of them.
+  const int per = (n_ct + 255) / 256;
+  const int j0 = min(tid * per, n_ct), j1 = min(j0 + per, n_ct);
+  int run = 0;
+  for (int j = j0; j < j1; ++j) run += cnt[j];
+  int total;
+  run = block256_exclusive_scan(run, sh, &total);
+  const int hit_base = rb * ROW_BLOCK * K;
+  int* off = hit_off + (long long)rb * n_ct;
+  for (int j = j0; j < j1; ++j) {
+    const int c = cnt[j];
+    cnt[j] = run;
+    off[j] = hit_base + run;
+    run += c;
+  }
+  __syncthreads();
+
+  // Placement: p is re-read from memory this workgroup wrote before the barrier.
+  for (int row = row_lo + wave; row < row_hi; row += 4) {
+    if (mask != nullptr && mask[row] == 0) continue;
+    const long long base = (long long)row * K;
+    for (int k = lane; k < K; k += 64) {
+      const int v = idx[base + k];
+      if (v >= 0 && v < V) {
+        const int pos = atomicAdd(&cnt[v / TILE_V], 1);
+        Hit h;
+        h.row = row;
+        h.k = k;
+        h.v = v;
+        h.p = p[base + k];
+        hits[hit_base + pos] = h;
+      }
+    }
+  }
 }
 
-// One thread per chunk row: merges the per-vocabulary-tile (max, sum-exp)
-// partials into the full-vocabulary LSE (fixed order, so the result does not
-// depend on the chunk size), then KL_t = E_t - sum_k p_k g_k + S_t * LSE_t.
+// 32 chunk rows per workgroup, 8 slices per row: slice s merges the
+// per-vocabulary-tile (max, sum-exp) partials j = s, s+8, ... and the teacher
+// terms k = s, s+8, ...; the slices are then combined in slice order.  The
+// merge order depends only on the number of vocabulary tiles, so LSE and KL do
+// not depend on the chunk size.  KL_t = E_t - sum_k p_k g_k + S_t * LSE_t.
+constexpr int kKlRows = 32, kKlSlices = 8;
 __global__ __launch_bounds__(256) void lse_kl_kernel(const float2* __restrict__ part, int ld_part,
                                                      int n_vt, int c0, int rows,
                                                      const float* __restrict__ p,
@@ -222,35 +172,51 @@ __global__ __launch_bounds__(256) void lse_kl_kernel(const float2* __restrict__ 
                                                      const uint8_t* __restrict__ mask, int K,
                                                      float* __restrict__ lse,
                                                      float* __restrict__ row_kl) {
-  const int r = blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= rows) return;
+  __shared__ float2 red[kKlSlices][kKlRows];
+  __shared__ float dred[kKlSlices][kKlRows];
+  const int rl = threadIdx.x % kKlRows, sl = threadIdx.x / kKlRows;
+  const int r = blockIdx.x * kKlRows + rl;
+  const bool ok = r < rows;
   const int t = c0 + r;
   float2 acc = make_float2(kNegInf, 0.f);
-  int j = 0;
-  for (; j + 4 <= n_vt; j += 4) {
-    float2 a = part[(long long)(j + 0) * ld_part + r];
-    float2 b = part[(long long)(j + 1) * ld_part + r];
-    float2 c = part[(long long)(j + 2) * ld_part + r];
-    float2 d = part[(long long)(j + 3) * ld_part + r];
-    acc = lse_merge(acc, a);
-    acc = lse_merge(acc, b);
-    acc = lse_merge(acc, c);
-    acc = lse_merge(acc, d);
+  if (ok) {
+    int j = sl;
+    for (; j + 3 * kKlSlices < n_vt; j += 4 * kKlSlices) {
+      const float2 a = part[(long long)j * ld_part + r];
+      const float2 b = part[(long long)(j + kKlSlices) * ld_part + r];
+      const float2 c = part[(long long)(j + 2 * kKlSlices) * ld_part + r];
+      const float2 d = part[(long long)(j + 3 * kKlSlices) * ld_part + r];
+      acc = lse_merge(acc, a);
+      acc = lse_merge(acc, b);
+      acc = lse_merge(acc, c);
+      acc = lse_merge(acc, d);
+    }
+    for (; j < n_vt; j += kKlSlices) acc = lse_merge(acc, part[(long long)j * ld_part + r]);
   }
-  for (; j < n_vt; ++j) acc = lse_merge(acc, part[(long long)j * ld_part + r]);
-  const float L = acc.x + logf(acc.y);
-  lse[t] = L;
-  float kl = 0.f;
-  if (mask == nullptr || mask[t] != 0) {
+  float dot = 0.f;
+  const bool live = ok && (mask == nullptr || mask[t] != 0);
+  if (live) {
     const long long base = (long long)t * K;
-    float dot = 0.f;
-    for (int k = 0; k < K; ++k) {
+    for (int k = sl; k < K; k += kKlSlices) {
       const float pk = p[base + k];
       dot += pk > 0.f ? pk * g[base + k] : 0.f;
     }
-    kl = E[t] - dot + S[t] * L;
   }
-  row_kl[t] = kl;
+  red[sl][rl] = acc;
+  dred[sl][rl] = dot;
+  __syncthreads();
+  if (sl == 0 && ok) {
+    float2 m = red[0][rl];
+    float dsum = dred[0][rl];
+#pragma unroll
+    for (int q = 1; q < kKlSlices; ++q) {
+      m = lse_merge(m, red[q][rl]);
+      dsum += dred[q][rl];
+    }
+    const float L = m.x + logf(m.y);
+    lse[t] = L;
+    row_kl[t] = live ? E[t] - dsum + S[t] * L : 0.f;
+  }
 }
 
 // Single block, fixed order: loss = sum_t row_kl[t] / N_valid (0 if none).
@@ -271,23 +237,53 @@ __global__ __launch_bounds__(1024) void loss_kernel(const float* __restrict__ ro
   }
 }
 
-// out[c][r] = in[r][c] for r < rows, 0 for rows <= r < rows_pad.  64x64 tiles.
+// out[c][r] = in[r][c] for r < rows, 0 for rows <= r < rows_pad.  64 x 64
+// tiles; rows of the tile move as 16-byte vectors in both directions (W of
+// element size es: 16/es elements per vector), through an LDS tile padded by
+// one 4-byte word per row.
 template <typename E>
 __global__ __launch_bounds__(256) void transpose_pad_kernel(const E* __restrict__ in, int rows,
                                                             int cols, long long ld_in,
                                                             E* __restrict__ out, int rows_pad,
                                                             long long ld_out) {
-  __shared__ E tile[64][65];
+  constexpr int EPV = 16 / sizeof(E);          // elements per 16-byte vector
+  constexpr int VPR = 64 / EPV;                // vectors per 64-element tile row
+  constexpr int PITCH = 64 + 4 / sizeof(E);    // tile row pitch in elements
+  __shared__ E tile[64 * PITCH];
   const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4) {
-    const int r = r0 + i, c = c0 + tx;
-    tile[i][tx] = (r < rows && c < cols) ? in[(long long)r * ld_in + c] : E(0);
+  const int tid = threadIdx.x;
+  const bool vec_in = (ld_in % EPV) == 0 && c0 + 64 <= cols;
+#pragma unroll
+  for (int q = tid; q < 64 * VPR; q += 256) {
+    const int i = q / VPR, cv = (q % VPR) * EPV;
+    const int r = r0 + i;
+    E v[EPV];
+    if (r < rows && vec_in) {
+      *reinterpret_cast<uint4*>(v) = *reinterpret_cast<const uint4*>(in + (long long)r * ld_in + c0 + cv);
+    } else {
+#pragma unroll
+      for (int u = 0; u < EPV; ++u) v[u] = (r < rows && c0 + cv + u < cols) ? in[(long long)r * ld_in + c0 + cv + u] : E(0);
+    }
+#pragma unroll
+    for (int u = 0; u < EPV; ++u) tile[i * PITCH + cv + u] = v[u];
   }
   __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int c = c0 + i, r = r0 + tx;
-    if (c < cols && r < rows_pad) out[(long long)c * ld_out + r] = tile[tx][i];
+  const bool vec_out = (ld_out % EPV) == 0 && r0 + 64 <= rows_pad;
+#pragma unroll
+  for (int q = tid; q < 64 * VPR; q += 256) {
+    const int cl = q / VPR, rv = (q % VPR) * EPV;
+    const int c = c0 + cl;
+    if (c >= cols) continue;
+    E v[EPV];
+#pragma unroll
+    for (int u = 0; u < EPV; ++u) v[u] = tile[(rv + u) * PITCH + cl];
+    if (vec_out) {
+      *reinterpret_cast<uint4*>(out + (long long)c * ld_out + r0 + rv) = *reinterpret_cast<const uint4*>(v);
+    } else {
+#pragma unroll
+      for (int u = 0; u < EPV; ++u)
+        if (r0 + rv + u < rows_pad) out[(long long)c * ld_out + r0 + rv + u] = v[u];
+    }
   }
 }
 
@@ -336,30 +332,21 @@ void launch_fill_i32(int* p, long long count, int value, hipStream_t s) {
   fill_i32_kernel<<<grid_for(count, 256, 4096), 256, 0, s>>>(p, count, value);
 }
 
-void launch_teacher_prep(const float* logp, const int* idx, const uint8_t* mask, int n, int K,
-                         int V, float* p, float* S, float* E, int* counts, int n_rb, Ctrl* ctrl,
-                         hipStream_t s) {
-  teacher_prep_kernel<<<(n + 3) / 4, 256, 0, s>>>(logp, idx, mask, n, K, V, p, S, E, counts, n_rb,
-                                                  ctrl);
-}
-
-void launch_scan(const int* counts, int n_keys, int* offsets, int* cursor, int* tmp, hipStream_t s) {
-  const int tiles = (n_keys + kScanTile - 1) / kScanTile;
-  scan_tiles_kernel<<<tiles, kScanThreads, 0, s>>>(counts, n_keys, tmp);
-  scan_totals_kernel<<<1, kScanThreads, 0, s>>>(tmp, tiles);
-  scan_apply_kernel<<<tiles, kScanThreads, 0, s>>>(counts, n_keys, tmp, offsets, cursor);
-}
-
-void launch_hit_scatter(const int* idx, const float* p, const uint8_t* mask, int n, int K, int V,
-                        int n_rb, int* cursor, Hit* hits, hipStream_t s) {
-  hit_scatter_kernel<<<(n + 3) / 4, 256, 0, s>>>(idx, p, mask, n, K, V, n_rb, cursor, hits);
+void launch_teacher_bucket(const float* logp, const int* idx, const uint8_t* mask, int n, int K,
+                           int V, float* p, float* S, float* E, int* hit_off, Hit* hits,
+                           Ctrl* ctrl, hipStream_t s) {
+  const int n_vt = (V + TILE_V - 1) / TILE_V;
+  const int n_rb = (n + ROW_BLOCK - 1) / ROW_BLOCK;
+  const size_t lds = size_t(n_vt + 1) * sizeof(int);
+  teacher_bucket_kernel<<<n_rb, 256, lds, s>>>(logp, idx, mask, n, K, V, n_vt, p, S, E, hit_off,
+                                               hits, ctrl);
 }
 
 void launch_lse_kl(const float2* part, int ld_part, int n_vt, int c0, int rows, const float* p,
                    const float* g, const float* S, const float* E, const uint8_t* mask, int K,
                    float* lse, float* row_kl, hipStream_t s) {
-  lse_kl_kernel<<<(rows + 255) / 256, 256, 0, s>>>(part, ld_part, n_vt, c0, rows, p, g, S, E, mask,
-                                                   K, lse, row_kl);
+  lse_kl_kernel<<<(rows + kKlRows - 1) / kKlRows, 256, 0, s>>>(part, ld_part, n_vt, c0, rows, p, g,
+                                                                S, E, mask, K, lse, row_kl);
 }
 
 void launch_loss(const float* row_kl, int n, const Ctrl* ctrl, float* loss, hipStream_t s) {
