@@ -71,7 +71,8 @@ def _load():
     lib.kd_fused_chunked_kl_fwd.argtypes = [
         ctypes.c_int, vp, vp, vp, vp, vp, i64, i64, i64, i32, i64, vp, sz, vp, vp, vp, vp, vp]
     lib.kd_fused_chunked_kl_bwd.argtypes = [
-        ctypes.c_int, vp, vp, vp, vp, vp, i64, i64, i64, i32, i64, vp, vp, vp, vp, vp, sz, vp]
+        ctypes.c_int, vp, vp, vp, vp, vp, i64, i64, i64, i32, i64, vp, vp, vp, vp, ctypes.c_int, vp, sz,
+        vp]
     lib.kd_status_string.argtypes = [ctypes.c_int]
     lib.kd_status_string.restype = ctypes.c_char_p
     lib.kd_last_error_message.argtypes = []
@@ -177,8 +178,10 @@ def kd_fused_chunked_kl_fwd(H, W, topk_idx, topk_logp, mask=None, chunk: int = 0
 
 
 def kd_fused_chunked_kl_bwd(H, W, topk_idx, topk_logp, mask, lse, grad_loss=None, chunk: int = 0,
-                            workspace=None, dW=None, plan: dict | None = None):
-    """Backward call.  Returns (dH, dW); dW is accumulated into when given."""
+                            workspace=None, dW=None, plan: dict | None = None, accumulate: bool = True):
+    """Backward call.  Returns (dH, dW).  A given dW is accumulated into
+    (accumulate=True) or overwritten (accumulate=False); without one, a new
+    dW is allocated and written."""
     n, d, V, K = _check_inputs(H, W, topk_idx, topk_logp, mask)
     dt = _dtype_code(H)
     plan = plan or kd_plan_query(dt, n, d, V, K, chunk)
@@ -188,13 +191,14 @@ def kd_fused_chunked_kl_bwd(H, W, topk_idx, topk_logp, mask, lse, grad_loss=None
     grad_loss = grad_loss.reshape(1).to(torch.float32).contiguous()
     dH = torch.empty_like(H)
     if dW is None:
-        dW = torch.zeros((V, d), dtype=torch.float32, device=H.device)
+        dW = torch.empty((V, d), dtype=torch.float32, device=H.device)
+        accumulate = False
     elif dW.dtype != torch.float32 or tuple(dW.shape) != (V, d) or not dW.is_contiguous():
         raise ValueError("dW must be a contiguous float32 [V, d] tensor")
     _check(lib().kd_fused_chunked_kl_bwd(
         dt, _ptr(H), _ptr(W), _ptr(topk_idx), _ptr(topk_logp), _ptr(mask), n, d, V, K,
-        plan["chunk"], _ptr(lse), _ptr(grad_loss), _ptr(dH), _ptr(dW), _ptr(ws),
-        ws.numel() * ws.element_size(), _stream(H.device)))
+        plan["chunk"], _ptr(lse), _ptr(grad_loss), _ptr(dH), _ptr(dW), 1 if accumulate else 0,
+        _ptr(ws), ws.numel() * ws.element_size(), _stream(H.device)))
     return dH, dW
 
 

@@ -129,7 +129,7 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 struct Layout {
   DType dt;
-  int64_t n, d, V, K, chunk, c_pad, v_pad, n_vt, n_rb, splits;
+  int64_t n, d, V, K, chunk, c_pad, v_pad, n_vt, n_rb, splits, n_chunks, gt_cols;
   // byte offsets
   size_t ctrl, p, S, E, hit_off, hits, common_end;
   size_t part, g, rowkl, fwd_end;
@@ -175,6 +175,9 @@ Layout make_layout(DType dt, int64_t n, int64_t d, int64_t V, int64_t K, int64_t
   L.n_vt = (V + kd::TILE_V - 1) / kd::TILE_V;
   L.n_rb = (n + kd::ROW_BLOCK - 1) / kd::ROW_BLOCK;
   L.splits = dh_splits(dt, L.c_pad, d, L.v_pad);
+  L.n_chunks = (n + chunk - 1) / chunk;
+  // G^T and H^T hold two chunks side by side, so dW runs once per pair of chunks.
+  L.gt_cols = L.n_chunks > 1 ? 2 * L.c_pad : L.c_pad;
   const size_t es = kd::elem_size(dt);
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -197,9 +200,9 @@ Layout make_layout(DType dt, int64_t n, int64_t d, int64_t V, int64_t K, int64_t
   // backward-only region (overlaps the forward-only one)
   o = L.common_end;
   L.G = take(size_t(L.c_pad) * L.v_pad * es);
-  L.GT = take(size_t(L.v_pad) * L.c_pad * es);
+  L.GT = take(size_t(L.v_pad) * L.gt_cols * es);
   L.WT = take(size_t(d) * L.v_pad * es);
-  L.HT = take(size_t(d) * L.c_pad * es);
+  L.HT = take(size_t(d) * L.gt_cols * es);
   L.dhpart = take(size_t(L.splits) * L.c_pad * d * 4);
   L.bwd_end = o;
   return L;
@@ -440,8 +443,8 @@ int kd_fused_chunked_kl_fwd(int dtype, const void* H, const void* W, const int32
 int kd_fused_chunked_kl_bwd(int dtype, const void* H, const void* W, const int32_t* topk_idx,
                             const float* topk_logp, const uint8_t* mask, int64_t n, int64_t d,
                             int64_t V, int32_t K, int64_t chunk, const float* lse,
-                            const float* grad_loss, void* dH, float* dW, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+                            const float* grad_loss, void* dH, float* dW, int accumulate_dw,
+                            void* workspace, size_t workspace_bytes, void* stream) {
   Layout L;
   int rc = plan(dtype, n, d, V, K, chunk, workspace_bytes ? workspace_bytes : 1, &L);
   if (rc != KD_OK) return rc;
@@ -459,15 +462,22 @@ int kd_fused_chunked_kl_bwd(int dtype, const void* H, const void* W, const int32
   KD_LAUNCH("transpose_w", 0, 2.0 * L.V * L.d * es,
             kd::launch_transpose_pad(L.dt, W, (int)L.V, (int)L.d, L.d, ws + L.WT, (int)L.v_pad,
                                      L.v_pad, s));
-  for (int64_t c0 = 0; c0 < L.n; c0 += L.chunk) {
+  bool dw_written = accumulate_dw != 0;  // later dW launches accumulate
+  int pair_rows = 0;                      // unpadded rows of the pair's chunks
+  for (int64_t c = 0; c < L.n_chunks; ++c) {
+    const int64_t c0 = c * L.chunk;
     const int rows = (int)std::min<int64_t>(L.chunk, L.n - c0);
     const int c_pad = (int)round_up(rows, kd::KPAD);
+    const int col0 = (int)((c % 2) * L.c_pad);  // this chunk's columns in G^T and H^T
     const char* Hc = static_cast<const char*>(H) + c0 * L.d * es;
     KD_LAUNCH("transpose_h", 0, 2.0 * rows * L.d * es,
-              kd::launch_transpose_pad(L.dt, Hc, rows, (int)L.d, L.d, ws + L.HT, c_pad, c_pad, s));
+              kd::launch_transpose_pad(L.dt, Hc, rows, (int)L.d, L.d, ws + L.HT + col0 * es, c_pad,
+                                       L.gt_cols, s));
     kd::RecomputeEpilogue ep{};
     ep.G = ws + L.G;
     ep.GT = ws + L.GT;
+    ep.gt_ld = (int)L.gt_cols;
+    ep.gt_col0 = col0;
     ep.v_pad = (int)L.v_pad;
     ep.c_pad = c_pad;
     ep.c0 = (int)c0;
@@ -496,9 +506,17 @@ int kd_fused_chunked_kl_bwd(int dtype, const void* H, const void* W, const int32
               kd::launch_dh_reduce(L.dt, reinterpret_cast<const float*>(ws + L.dhpart),
                                    (int)L.splits, split_stride, rows, (int)L.d,
                                    static_cast<char*>(dH) + c0 * L.d * es, s));
-    KD_LAUNCH("dw_gemm", fl,
-              double(L.V) * c_pad * es + double(L.d) * c_pad * es + 2.0 * L.V * L.d * 4,
-              kd::launch_dw_gemm(L.dt, ws + L.GT, (int)L.V, c_pad, ws + L.HT, (int)L.d, dW, s));
+    pair_rows += rows;
+    if (c % 2 == 1 || c == L.n_chunks - 1) {
+      const int k_len = col0 + c_pad;
+      KD_LAUNCH("dw_gemm", 2.0 * pair_rows * L.d * L.V,
+                double(L.V) * k_len * es + double(L.d) * k_len * es +
+                    (dw_written ? 2.0 : 1.0) * L.V * L.d * 4,
+                kd::launch_dw_gemm(L.dt, ws + L.GT, (int)L.V, k_len, L.gt_cols, ws + L.HT, (int)L.d,
+                                   L.gt_cols, dW, dw_written, s));
+      dw_written = true;
+      pair_rows = 0;
+    }
   }
   return ok();
 }

@@ -44,6 +44,7 @@ struct Traits<float> {
 static_assert(Traits<__bf16>::BK * 2 == ROWB && Traits<float>::BK * 4 == ROWB, "K block is one staged row");
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Buffer resource of a raw (stride 0) buffer of num_records bytes at base.
 __device__ inline i32x4 make_rsrc(const void* base, unsigned num_records) {
@@ -367,8 +368,10 @@ struct KLoop {
   }
 };
 
+// Forced inline: several kernels instantiate the same main loop and epilogue,
+// and an out-of-line call would pass the accumulators through scratch memory.
 template <typename T, int BN, int WC>
-__device__ inline void gemm_mainloop(const Operand& A, const Operand& B, int k_elems, int tm, int tn,
+__device__ __attribute__((always_inline)) inline void gemm_mainloop(const Operand& A, const Operand& B, int k_elems, int tm, int tn,
                                      int kb0, int kb1, char* lds,
                                      f32x16 (&acc)[4][BN / (32 * WC)]) {
   using ML = MainLoop<T, BN, WC>;
@@ -685,13 +688,14 @@ __global__ __launch_bounds__(kFusedThreads, 1) void recompute_gemm_kernel(Operan
             const int n2 = n & ~1;
             T pr[2] = {(T)(odd ? y1 : x0), (T)(odd ? x1 : y0)};
             if (v < ep.v_pad && n2 < ep.c_pad)
-              *reinterpret_cast<uint32_t*>(GT + (long long)v * ep.c_pad + n2) =
-                  *reinterpret_cast<const uint32_t*>(pr);
+              __builtin_nontemporal_store(*reinterpret_cast<const uint32_t*>(pr),
+                                          reinterpret_cast<uint32_t*>(GT + (long long)v * ep.gt_ld + ep.gt_col0 + n2));
           }
         } else {
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            if (v0 + j < ep.v_pad && n < ep.c_pad) GT[(long long)(v0 + j) * ep.c_pad + n] = (T)acc[bi][bj][4 * i + j];
+            if (v0 + j < ep.v_pad && n < ep.c_pad)
+              __builtin_nontemporal_store((T)acc[bi][bj][4 * i + j], GT + (long long)(v0 + j) * ep.gt_ld + ep.gt_col0 + n);
         }
       }
     }
@@ -724,7 +728,8 @@ __global__ __launch_bounds__(kFusedThreads, 1) void recompute_gemm_kernel(Operan
       const uint4 val = *reinterpret_cast<const uint4*>(reg + row * kPitch + c * 16);
       const int n = n_wave + bj * 32 + row;
       const int v = v_wave + c * EPC;
-      if (n < ep.c_pad && v < ep.v_pad) *reinterpret_cast<uint4*>(G + (long long)n * ep.v_pad + v) = val;
+      if (n < ep.c_pad && v < ep.v_pad)
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, val), reinterpret_cast<u32x4*>(G + (long long)n * ep.v_pad + v));
     }
   }
 }
@@ -738,7 +743,7 @@ constexpr int kPlainWC = KD_PLAIN_WC;          // wavefront columns of the dH / 
 constexpr int kPlainThreads = 128 * kPlainWC;
 
 template <typename T, bool kAccumulate>
-__device__ inline void plain_gemm(char* lds, Operand A, Operand B, int k_elems, int tiles_m,
+__device__ __attribute__((always_inline)) inline void plain_gemm(char* lds, Operand A, Operand B, int k_elems, int tiles_m,
                                   int tiles_n, int splits, int kb_per_split, float* out,
                                   long long ld_out, long long split_stride, int M, int N) {
   constexpr int BN = TILE_D, WC = kPlainWC, NBJ = BN / (32 * WC);
@@ -817,13 +822,14 @@ __global__ __launch_bounds__(kPlainThreads, 1) void dh_gemm_kernel(Operand A, Op
                        split_stride, M, N);
 }
 
-template <typename T>
+template <typename T, bool kAccumulate>
 __global__ __launch_bounds__(kPlainThreads, 1) void dw_gemm_kernel(Operand A, Operand B, int k_elems,
                                                                     int tiles_m, int tiles_n,
                                                                     int kb_per_split, float* out,
                                                                     long long ld_out, int M, int N) {
   KD_DECLARE_LDS(TILE_D);
-  plain_gemm<T, true>(lds, A, B, k_elems, tiles_m, tiles_n, 1, kb_per_split, out, ld_out, 0, M, N);
+  plain_gemm<T, kAccumulate>(lds, A, B, k_elems, tiles_m, tiles_n, 1, kb_per_split, out, ld_out, 0,
+                             M, N);
 }
 
 template <typename T>
@@ -886,20 +892,25 @@ void launch_dh_gemm(DType t, const void* G, int rows, int v_pad, const void* WT,
         tiles_n, splits, kb_per, part, d, split_stride, rows, d);
 }
 
-void launch_dw_gemm(DType t, const void* GT, int V, int c_pad, const void* HT, int d, float* dW,
-                    hipStream_t s) {
+template <typename T, bool kAcc>
+void dw_impl(const void* GT, int V, int k_len, long long ld_gt, const void* HT, int d, long long ld_ht,
+             float* dW, hipStream_t s) {
   const int tiles_m = (V + BM - 1) / BM, tiles_n = (d + TILE_D - 1) / TILE_D;
-  const int bk = k_block(t);
-  const int kb_total = (c_pad + bk - 1) / bk;
-  const int grid = tiles_m * tiles_n;
-  if (t == DType::BF16)
-    dw_gemm_kernel<__bf16><<<grid, kPlainThreads, 0, s>>>(
-        make_operand<__bf16>(GT, c_pad, V), make_operand<__bf16>(HT, c_pad, d), c_pad, tiles_m,
-        tiles_n, kb_total, dW, d, V, d);
-  else
-    dw_gemm_kernel<float><<<grid, kPlainThreads, 0, s>>>(
-        make_operand<float>(GT, c_pad, V), make_operand<float>(HT, c_pad, d), c_pad, tiles_m,
-        tiles_n, kb_total, dW, d, V, d);
+  const int kb_total = (k_len + Traits<T>::BK - 1) / Traits<T>::BK;
+  dw_gemm_kernel<T, kAcc><<<tiles_m * tiles_n, kPlainThreads, 0, s>>>(
+      make_operand<T>(GT, ld_gt, V), make_operand<T>(HT, ld_ht, d), k_len, tiles_m, tiles_n, kb_total,
+      dW, d, V, d);
+}
+
+void launch_dw_gemm(DType t, const void* GT, int V, int k_len, long long ld_gt, const void* HT, int d,
+                    long long ld_ht, float* dW, bool accumulate, hipStream_t s) {
+  if (t == DType::BF16) {
+    if (accumulate) dw_impl<__bf16, true>(GT, V, k_len, ld_gt, HT, d, ld_ht, dW, s);
+    else dw_impl<__bf16, false>(GT, V, k_len, ld_gt, HT, d, ld_ht, dW, s);
+  } else {
+    if (accumulate) dw_impl<float, true>(GT, V, k_len, ld_gt, HT, d, ld_ht, dW, s);
+    else dw_impl<float, false>(GT, V, k_len, ld_gt, HT, d, ld_ht, dW, s);
+  }
 }
 
 }  // namespace kd

@@ -78,7 +78,9 @@ struct FwdEpilogue {
 
 struct RecomputeEpilogue {
   void* G;             // [c_pad][v_pad] dtype
-  void* GT;            // [v_pad][c_pad] dtype
+  void* GT;            // [v_pad][gt_ld] dtype; this chunk's columns start at gt_col0
+  int gt_ld;
+  int gt_col0;
   int v_pad;
   int c_pad;
   int c0;
@@ -105,8 +107,9 @@ void launch_recompute_gemm(DType t, const void* W, int V, const void* Hc, int ro
 // part[split][c_pad][d] = G[:, split range] * W^T[split range, :]  (fp32 partials)
 void launch_dh_gemm(DType t, const void* G, int rows, int v_pad, const void* WT, int d,
                     int splits, float* part, long long split_stride, hipStream_t s);
-// dW[V][d] += G^T * H_c
-void launch_dw_gemm(DType t, const void* GT, int V, int c_pad, const void* HT, int d, float* dW,
-                    hipStream_t s);
+// dW[V][d] (+)= G^T * H over k_len token columns (G^T rows of pitch ld_gt,
+// H^T rows of pitch ld_ht); accumulate == false overwrites dW.
+void launch_dw_gemm(DType t, const void* GT, int V, int k_len, long long ld_gt, const void* HT, int d,
+                    long long ld_ht, float* dW, bool accumulate, hipStream_t s);
 
 }  // namespace kd

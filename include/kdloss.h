@@ -107,19 +107,22 @@ int kd_fused_chunked_kl_fwd(int dtype, const void* H, const void* W, const int32
 
 /*
  * Backward: recomputes each chunk's logits from H and W, forms G in registers
- * (rounded to the input dtype), then dH = G W and dW += G^T H.
+ * (rounded to the input dtype), then dH = G W and dW (+)= G^T H.
  *   lse       [n] fp32 device: exactly what kd_fused_chunked_kl_fwd wrote
  *   grad_loss [1] fp32 device: upstream gradient of the loss (1 for plain training)
  *   dH        [n, d] dtype device: OVERWRITTEN (rows of masked positions are 0)
- *   dW        [V, d] fp32 device: ACCUMULATED (+=); the caller zeroes it first
+ *   dW        [V, d] fp32 device: accumulate_dw != 0: ACCUMULATED (+=) into
+ *             the caller's values; accumulate_dw == 0: OVERWRITTEN (every
+ *             element written, prior contents never read, so it may be
+ *             uninitialised)
  *   workspace: at least plan.bwd_workspace_bytes.
  * No gradient is produced for the teacher inputs.
  */
 int kd_fused_chunked_kl_bwd(int dtype, const void* H, const void* W, const int32_t* topk_idx,
                             const float* topk_logp, const uint8_t* mask, int64_t n, int64_t d,
                             int64_t V, int32_t K, int64_t chunk, const float* lse,
-                            const float* grad_loss, void* dH, float* dW, void* workspace,
-                            size_t workspace_bytes, void* stream);
+                            const float* grad_loss, void* dH, float* dW, int accumulate_dw,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* kd_status_string(int status);

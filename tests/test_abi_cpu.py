@@ -112,5 +112,5 @@ def test_null_pointers_rejected_without_device_work():
     assert rc == -2 and b"workspace" in lib.kd_last_error_message()
     misaligned = ctypes.c_void_p(4104)
     rc = lib.kd_fused_chunked_kl_bwd(0, misaligned, fake, fake, fake, None, 256, 256, 4096, 16, 64,
-                                     fake, fake, fake, fake, fake, 1 << 30, None)
+                                     fake, fake, fake, fake, 1, fake, 1 << 30, None)
     assert rc == -1 and b"aligned" in lib.kd_last_error_message()

@@ -118,6 +118,26 @@ def test_deterministic_repeat():
         assert np.array_equal(a[k], b[k]), k
 
 
+@pytest.mark.parametrize("chunk", [520, 192, 128])
+def test_dw_overwrite_mode(chunk):
+    """accumulate=False never reads dW (NaN-filled here) and matches a fresh
+    result bit for bit; so does accumulating onto zeros.  192 and 128 give 3
+    and 5 chunks: the G^T pairs end on a lone chunk."""
+    inp = synth.make_custom(520, 64, 1100, 12, "bf16", "random5", "uniform", seed=15)
+    d = {k: v.cuda() for k, v in inp.items() if torch.is_tensor(v)}
+    fw = kd.kd_fused_chunked_kl_fwd(d["H"], d["W"], d["idx"], d["logp"], d["mask"], chunk=chunk)
+    args = (d["H"], d["W"], d["idx"], d["logp"], d["mask"], fw["lse"])
+    _, dw_new = kd.kd_fused_chunked_kl_bwd(*args, plan=fw["plan"])
+    nan = torch.full_like(dw_new, float("nan"))
+    _, dw_over = kd.kd_fused_chunked_kl_bwd(*args, dW=nan, plan=fw["plan"], accumulate=False)
+    zero = torch.zeros_like(dw_new)
+    _, dw_acc = kd.kd_fused_chunked_kl_bwd(*args, dW=zero, plan=fw["plan"], accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dw_new, dw_over) and torch.equal(dw_new, dw_acc)
+    b = O.backward(inp["H"], inp["W"], inp["idx"].numpy(), inp["logp"], inp["mask"].numpy())
+    assert rel_fro(dw_new.cpu().double().numpy(), b["dW"]) <= 1e-2
+
+
 @pytest.mark.parametrize("chunk", [300, 128])
 def test_dw_accumulates_and_grad_scales(chunk):
     inp = synth.make_custom(300, 64, 900, 12, "bf16", "random5", "uniform", seed=14)
