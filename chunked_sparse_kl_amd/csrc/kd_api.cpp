@@ -129,7 +129,7 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 struct Layout {
   DType dt;
-  int64_t n, d, V, K, chunk, c_pad, v_pad, n_vt, n_rb, splits, n_chunks, gt_cols;
+  int64_t n, d, V, K, chunk, c_pad, v_pad, n_vt, n_rb, splits, n_chunks, gt_cols, g_rows;
   // byte offsets
   size_t ctrl, p, S, E, hit_off, hits, common_end;
   size_t part, g, rowkl, fwd_end;
@@ -199,8 +199,11 @@ Layout make_layout(DType dt, int64_t n, int64_t d, int64_t V, int64_t K, int64_t
   L.fwd_end = o;
   // backward-only region (overlaps the forward-only one)
   o = L.common_end;
-  L.G = take(size_t(L.c_pad) * L.v_pad * es);
-  L.GT = take(size_t(L.v_pad) * L.gt_cols * es);
+  // bf16: G holds the pair of chunks and dW reads it k-major (no G^T);
+  // fp32: G holds one chunk and dW reads G^T.
+  L.g_rows = L.dt == DType::BF16 ? L.gt_cols : L.c_pad;
+  L.G = take(size_t(L.g_rows) * L.v_pad * es);
+  L.GT = L.dt == DType::BF16 ? o : take(size_t(L.v_pad) * L.gt_cols * es);
   L.WT = take(size_t(d) * L.v_pad * es);
   L.HT = take(size_t(d) * L.gt_cols * es);
   L.dhpart = take(size_t(L.splits) * L.c_pad * d * 4);
@@ -473,9 +476,12 @@ int kd_fused_chunked_kl_bwd(int dtype, const void* H, const void* W, const int32
     KD_LAUNCH("transpose_h", 0, 2.0 * rows * L.d * es,
               kd::launch_transpose_pad(L.dt, Hc, rows, (int)L.d, L.d, ws + L.HT + col0 * es, c_pad,
                                        L.gt_cols, s));
+    const bool kmajor = L.dt == DType::BF16;  // dW reads G itself
+    const int g_row0 = kmajor ? col0 : 0;
     kd::RecomputeEpilogue ep{};
     ep.G = ws + L.G;
-    ep.GT = ws + L.GT;
+    ep.GT = kmajor ? nullptr : ws + L.GT;
+    ep.g_row0 = g_row0;
     ep.gt_ld = (int)L.gt_cols;
     ep.gt_col0 = col0;
     ep.v_pad = (int)L.v_pad;
@@ -499,7 +505,8 @@ int kd_fused_chunked_kl_bwd(int dtype, const void* H, const void* W, const int32
     const long long split_stride = (long long)L.c_pad * L.d;
     KD_LAUNCH("dh_gemm", fl,
               double(c_pad) * L.v_pad * es + double(L.d) * L.v_pad * es + double(L.splits) * rows * L.d * 4,
-              kd::launch_dh_gemm(L.dt, ws + L.G, rows, (int)L.v_pad, ws + L.WT, (int)L.d,
+              kd::launch_dh_gemm(L.dt, ws + L.G + size_t(g_row0) * L.v_pad * es, rows, (int)L.v_pad,
+                                 ws + L.WT, (int)L.d,
                                  (int)L.splits, reinterpret_cast<float*>(ws + L.dhpart),
                                  split_stride, s));
     KD_LAUNCH("dh_reduce", 0, double(L.splits) * rows * L.d * 4 + double(rows) * L.d * es,
@@ -512,8 +519,10 @@ int kd_fused_chunked_kl_bwd(int dtype, const void* H, const void* W, const int32
       KD_LAUNCH("dw_gemm", 2.0 * pair_rows * L.d * L.V,
                 double(L.V) * k_len * es + double(L.d) * k_len * es +
                     (dw_written ? 2.0 : 1.0) * L.V * L.d * 4,
-                kd::launch_dw_gemm(L.dt, ws + L.GT, (int)L.V, k_len, L.gt_cols, ws + L.HT, (int)L.d,
-                                   L.gt_cols, dW, dw_written, s));
+                kmajor ? kd::launch_dw_gemm_kmajor(ws + L.G, (int)L.V, (int)L.v_pad, k_len, L.v_pad,
+                                                   ws + L.HT, (int)L.d, L.gt_cols, dW, dw_written, s)
+                       : kd::launch_dw_gemm(L.dt, ws + L.GT, (int)L.V, k_len, L.gt_cols, ws + L.HT,
+                                            (int)L.d, L.gt_cols, dW, dw_written, s));
       dw_written = true;
       pair_rows = 0;
     }

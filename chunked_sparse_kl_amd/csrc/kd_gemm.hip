@@ -158,8 +158,14 @@ struct Operand {
 // results are never stored).  The one K block that runs past the contraction
 // end is loaded through registers with ordinary buffer loads, whose
 // out-of-range chunks read as zero.
-template <typename T, int BN, int WC>
+// kAT: A is stored k-major ([k][m], m contiguous; bf16 only).  Its K block is
+// then 64 staged rows of BM elements (512 bytes): one load instruction fills
+// two such rows, 16-byte chunk c of row k sits at c ^ 4 (k % 4), and the MFMA
+// fragments come from transposing LDS reads (ds_read_b64_tr_b16).  The block's
+// buffer resource is rebased per K block, so the operand may exceed 4 GB.
+template <typename T, int BN, int WC, bool kAT = false>
 struct MainLoop {
+  static_assert(!kAT || sizeof(T) == 2, "k-major A needs 16-bit elements");
   static constexpr int BK = Traits<T>::BK;
   static constexpr int EPC = 16 / sizeof(T);      // elements per 16-byte chunk
   static constexpr int WAVES = 2 * WC;            // 2 wavefront rows x WC columns
@@ -182,6 +188,7 @@ struct MainLoop {
   int c;                     // logical chunk fetched by this lane
   int k_elems;
   int wave_row;              // wave * 8 (uniform)
+  long long a_ld;            // kAT: bytes per k row of A
 
   __device__ inline void init(const Operand& A, const Operand& B, int ke, int tm, int tn) {
     const int lane = threadIdx.x & 63;
@@ -190,6 +197,24 @@ struct MainLoop {
     r = lane >> 3;
     c = (lane & 7) ^ (((wave_row + r) >> 1) & 7);
     k_elems = ke;
+    if constexpr (kAT) {
+      // A.rows is the m extent; lane L of load i stages k row 16 i + 2 w + L / 32,
+      // physical chunk L % 32, i.e. logical chunk (L % 32) ^ 4 (row % 4).
+      const int row = 2 * w + (lane >> 5);
+      const int ca = (lane & 31) ^ (4 * (row & 3));
+      a_valid = min(A.rows - tm * BM, BM);
+      a_tile = A.base + (long long)tm * BM * (long long)sizeof(T);
+      a_ld = A.ld;
+      a_off = (ca * EPC < a_valid) ? (unsigned)(row * A.ld + ca * 16) : kOut;
+      a_step = (unsigned)(16 * A.ld);
+      b_valid = min(B.rows - tn * BN, BN);
+      b_tile = B.base + (long long)tn * BN * B.ld;
+      b_bytes = (unsigned)(b_valid * B.ld);
+      rb = make_rsrc(b_tile, b_bytes);
+      b_off = (unsigned)((wave_row + r) * B.ld + c * 16);
+      b_step = (unsigned)(ROWS_PER_LD * B.ld);
+      return;
+    }
     a_valid = min(A.rows - tm * BM, BM);
     b_valid = min(B.rows - tn * BN, BN);
     a_tile = A.base + (long long)tm * BM * A.ld;
@@ -209,6 +234,12 @@ struct MainLoop {
   // range: the instruction still counts in vmcnt (so every step waits for the
   // same count) but reads nothing.
   __device__ inline void issue_a(int kb, char* st, bool valid, int i) const {
+    if constexpr (kAT) {
+      const i32x4 rk = make_rsrc(a_tile + (long long)kb * BK * a_ld, (unsigned)(BK * a_ld));
+      const unsigned off = (valid && a_off != kOut) ? a_off + i * a_step : kOut;
+      dma16(rk, off, __builtin_amdgcn_readfirstlane(lds_addr(st + (16 * i + wave_row / 4) * BM * (int)sizeof(T))));
+      return;
+    }
     const unsigned off = (valid && wave_row + r + ROWS_PER_LD * i < a_valid) ? a_off + i * a_step + (unsigned)kb * ROWB : kOut;
     dma16(ra, off, __builtin_amdgcn_readfirstlane(lds_addr(st + (i * ROWS_PER_LD + wave_row) * ROWB)));
   }
@@ -259,13 +290,35 @@ struct MainLoop {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wr = wave / WC, wc = wave % WC;
     const int r32 = lane & 31, h = lane >> 5;
-    const char* a_row0 = sa + (wr * 128 + r32) * ROWB;
     const char* b_row0 = sb + (wc * (BN / WC) + r32) * ROWB;
     const int ch = ((2 * s + h) ^ ((r32 >> 1) & 7)) << 4;
 #pragma unroll
     for (int bj = 0; bj < NBJ; ++bj) f.b[bj] = *reinterpret_cast<const uint4*>(b_row0 + bj * 32 * ROWB + ch);
+    if constexpr (kAT) {
+      // Lane l of 16-lane group g names k row kb + (l%16)/4 and columns
+      // m0 + 4 (l % 4) .. +3; the transposing read hands lane i of the group
+      // the 4 k values of column m0 + i.  Two reads give k = 16 s + 8 h .. +7.
+      // k % 4 = (l % 16) / 4 for every read, so the swizzle term depends on
+      // the lane and bi only and the rest is an immediate offset.
+      const int g = lane >> 4, q = lane & 15, x = q >> 2;
+      const int m = wr * 128 + 16 * (g & 1) + 4 * (q & 3);
+      const unsigned base = lds_addr(sa) + (unsigned)((8 * (g >> 1) + x) * (BM * 2) + (m & 7) * 2);
+      typedef short v4s __attribute__((ext_vector_type(4)));
 #pragma unroll
-    for (int bi = 0; bi < 4; ++bi) f.a[bi] = *reinterpret_cast<const uint4*>(a_row0 + bi * 32 * ROWB + ch);
+      for (int bi = 0; bi < 4; ++bi) {
+        const unsigned a = base + ((((m >> 3) + 4 * bi) ^ (4 * x)) << 4);
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s*)(a + (16 * s) * (BM * 2)));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s*)(a + (16 * s + 4) * (BM * 2)));
+        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+        f.a[bi] = uint4{l2.x, l2.y, h2.x, h2.y};
+      }
+    } else {
+      const char* a_row0 = sa + (wr * 128 + r32) * ROWB;
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi) f.a[bi] = *reinterpret_cast<const uint4*>(a_row0 + bi * 32 * ROWB + ch);
+    }
   }
 
   __device__ inline static void mma(const Frags& f, f32x16 (&acc)[4][NBJ]) {
@@ -314,9 +367,9 @@ struct Slots {
   __device__ inline char* b(int i) const { return lds + 3 * Smem<BN>::kA + i * Smem<BN>::kB; }
 };
 
-template <typename T, int BN, int WC>
+template <typename T, int BN, int WC, bool kAT = false>
 struct KLoop {
-  using ML = MainLoop<T, BN, WC>;
+  using ML = MainLoop<T, BN, WC, kAT>;
   ML ml;
   Slots<BN> sl;
   int kb_full;
@@ -370,18 +423,18 @@ struct KLoop {
 
 // Forced inline: several kernels instantiate the same main loop and epilogue,
 // and an out-of-line call would pass the accumulators through scratch memory.
-template <typename T, int BN, int WC>
+template <typename T, int BN, int WC, bool kAT = false>
 __device__ __attribute__((always_inline)) inline void gemm_mainloop(const Operand& A, const Operand& B, int k_elems, int tm, int tn,
                                      int kb0, int kb1, char* lds,
                                      f32x16 (&acc)[4][BN / (32 * WC)]) {
-  using ML = MainLoop<T, BN, WC>;
+  using ML = MainLoop<T, BN, WC, kAT>;
 #pragma unroll
   for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
     for (int bj = 0; bj < ML::NBJ; ++bj)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[bi][bj][e] = 0.f;
-  KLoop<T, BN, WC> L;
+  KLoop<T, BN, WC, kAT> L;
   L.sl.lds = lds;
   L.ml.init(A, B, k_elems, tm, tn);
   L.kb_full = min(kb1, k_elems / ML::BK);  // blocks entirely inside the contraction
@@ -411,7 +464,7 @@ __device__ __attribute__((always_inline)) inline void gemm_mainloop(const Operan
   if (kb + 4 < kb_full) L.template step<4>(kb + 4, acc);
   wait_vmcnt<0>();      // the trailing out-of-range loads, before LDS is reused
   __syncthreads();
-  if (kb_full < kb1) {  // ragged last block (at most one)
+  if (!kAT && kb_full < kb1) {  // ragged last block (at most one; never with k-major A)
     char* const sa = L.sl.a(0);
     char* const sb = L.sl.b(0);
     L.ml.load_ragged(kb_full, sa, sb);
@@ -666,9 +719,11 @@ __global__ __launch_bounds__(kFusedThreads, 1) void recompute_gemm_kernel(Operan
 
   T* G = static_cast<T*>(ep.G);
   T* GT = static_cast<T*>(ep.GT);
-  // --- G^T[v][n]: for a fixed register, the 32 lanes of a half-wavefront
+  // --- G^T[v][n] (only when the dW GEMM reads G^T rather than G itself): for
+  // a fixed register, the 32 lanes of a half-wavefront
   // hold 32 consecutive tokens of one vocabulary row.  bf16: neighbouring
   // lanes swap values so each lane stores two tokens (4 bytes).
+  if (GT != nullptr) {
 #pragma unroll
   for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
@@ -699,6 +754,7 @@ __global__ __launch_bounds__(kFusedThreads, 1) void recompute_gemm_kernel(Operan
         }
       }
     }
+  }
   // --- G[n][v]: each wavefront stages its 32-token x 128-row blocks (rounded
   // to T) in its own LDS rows and stores whole 128-value rows.
   constexpr int kPitch = 128 * (int)sizeof(T) + 16;    // bytes per staged token row
@@ -729,7 +785,8 @@ __global__ __launch_bounds__(kFusedThreads, 1) void recompute_gemm_kernel(Operan
       const int n = n_wave + bj * 32 + row;
       const int v = v_wave + c * EPC;
       if (n < ep.c_pad && v < ep.v_pad)
-        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, val), reinterpret_cast<u32x4*>(G + (long long)n * ep.v_pad + v));
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, val),
+                                    reinterpret_cast<u32x4*>(G + (long long)(ep.g_row0 + n) * ep.v_pad + v));
     }
   }
 }
@@ -742,7 +799,7 @@ __global__ __launch_bounds__(kFusedThreads, 1) void recompute_gemm_kernel(Operan
 constexpr int kPlainWC = KD_PLAIN_WC;          // wavefront columns of the dH / dW tiles
 constexpr int kPlainThreads = 128 * kPlainWC;
 
-template <typename T, bool kAccumulate>
+template <typename T, bool kAccumulate, bool kAT = false>
 __device__ __attribute__((always_inline)) inline void plain_gemm(char* lds, Operand A, Operand B, int k_elems, int tiles_m,
                                   int tiles_n, int splits, int kb_per_split, float* out,
                                   long long ld_out, long long split_stride, int M, int N) {
@@ -752,7 +809,7 @@ __device__ __attribute__((always_inline)) inline void plain_gemm(char* lds, Oper
   const int kb0 = ti.split * kb_per_split;
   const int kb1 = min(kb0 + kb_per_split, kb_total);
   f32x16 acc[4][NBJ];
-  gemm_mainloop<T, BN, WC>(A, B, k_elems, ti.tm, ti.tn, kb0, kb1, lds, acc);
+  gemm_mainloop<T, BN, WC, kAT>(A, B, k_elems, ti.tm, ti.tn, kb0, kb1, lds, acc);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave / WC, wc = wave % WC, r32 = lane & 31, h = lane >> 5;
@@ -822,14 +879,14 @@ __global__ __launch_bounds__(kPlainThreads, 1) void dh_gemm_kernel(Operand A, Op
                        split_stride, M, N);
 }
 
-template <typename T, bool kAccumulate>
+template <typename T, bool kAccumulate, bool kAT>
 __global__ __launch_bounds__(kPlainThreads, 1) void dw_gemm_kernel(Operand A, Operand B, int k_elems,
                                                                     int tiles_m, int tiles_n,
                                                                     int kb_per_split, float* out,
                                                                     long long ld_out, int M, int N) {
   KD_DECLARE_LDS(TILE_D);
-  plain_gemm<T, kAccumulate>(lds, A, B, k_elems, tiles_m, tiles_n, 1, kb_per_split, out, ld_out, 0,
-                             M, N);
+  plain_gemm<T, kAccumulate, kAT>(lds, A, B, k_elems, tiles_m, tiles_n, 1, kb_per_split, out, ld_out,
+                                  0, M, N);
 }
 
 template <typename T>
@@ -892,25 +949,31 @@ void launch_dh_gemm(DType t, const void* G, int rows, int v_pad, const void* WT,
         tiles_n, splits, kb_per, part, d, split_stride, rows, d);
 }
 
-template <typename T, bool kAcc>
-void dw_impl(const void* GT, int V, int k_len, long long ld_gt, const void* HT, int d, long long ld_ht,
-             float* dW, hipStream_t s) {
+template <typename T, bool kAcc, bool kAT>
+void dw_impl(const void* A, int V, int a_rows, int k_len, long long ld_a, const void* HT, int d,
+             long long ld_ht, float* dW, hipStream_t s) {
   const int tiles_m = (V + BM - 1) / BM, tiles_n = (d + TILE_D - 1) / TILE_D;
   const int kb_total = (k_len + Traits<T>::BK - 1) / Traits<T>::BK;
-  dw_gemm_kernel<T, kAcc><<<tiles_m * tiles_n, kPlainThreads, 0, s>>>(
-      make_operand<T>(GT, ld_gt, V), make_operand<T>(HT, ld_ht, d), k_len, tiles_m, tiles_n, kb_total,
-      dW, d, V, d);
+  dw_gemm_kernel<T, kAcc, kAT><<<tiles_m * tiles_n, kPlainThreads, 0, s>>>(
+      make_operand<T>(A, ld_a, a_rows), make_operand<T>(HT, ld_ht, d), k_len, tiles_m, tiles_n,
+      kb_total, dW, d, V, d);
 }
 
 void launch_dw_gemm(DType t, const void* GT, int V, int k_len, long long ld_gt, const void* HT, int d,
                     long long ld_ht, float* dW, bool accumulate, hipStream_t s) {
   if (t == DType::BF16) {
-    if (accumulate) dw_impl<__bf16, true>(GT, V, k_len, ld_gt, HT, d, ld_ht, dW, s);
-    else dw_impl<__bf16, false>(GT, V, k_len, ld_gt, HT, d, ld_ht, dW, s);
+    if (accumulate) dw_impl<__bf16, true, false>(GT, V, V, k_len, ld_gt, HT, d, ld_ht, dW, s);
+    else dw_impl<__bf16, false, false>(GT, V, V, k_len, ld_gt, HT, d, ld_ht, dW, s);
   } else {
-    if (accumulate) dw_impl<float, true>(GT, V, k_len, ld_gt, HT, d, ld_ht, dW, s);
-    else dw_impl<float, false>(GT, V, k_len, ld_gt, HT, d, ld_ht, dW, s);
+    if (accumulate) dw_impl<float, true, false>(GT, V, V, k_len, ld_gt, HT, d, ld_ht, dW, s);
+    else dw_impl<float, false, false>(GT, V, V, k_len, ld_gt, HT, d, ld_ht, dW, s);
   }
+}
+
+void launch_dw_gemm_kmajor(const void* G, int V, int v_pad, int k_len, long long ld_g, const void* HT,
+                           int d, long long ld_ht, float* dW, bool accumulate, hipStream_t s) {
+  if (accumulate) dw_impl<__bf16, true, true>(G, V, v_pad, k_len, ld_g, HT, d, ld_ht, dW, s);
+  else dw_impl<__bf16, false, true>(G, V, v_pad, k_len, ld_g, HT, d, ld_ht, dW, s);
 }
 
 }  // namespace kd

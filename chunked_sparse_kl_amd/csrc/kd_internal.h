@@ -77,8 +77,9 @@ struct FwdEpilogue {
 };
 
 struct RecomputeEpilogue {
-  void* G;             // [c_pad][v_pad] dtype
-  void* GT;            // [v_pad][gt_ld] dtype; this chunk's columns start at gt_col0
+  void* G;             // [*][v_pad] dtype; this chunk's rows start at g_row0
+  void* GT;            // [v_pad][gt_ld] dtype or null; this chunk's columns start at gt_col0
+  int g_row0;
   int gt_ld;
   int gt_col0;
   int v_pad;
@@ -111,5 +112,9 @@ void launch_dh_gemm(DType t, const void* G, int rows, int v_pad, const void* WT,
 // H^T rows of pitch ld_ht); accumulate == false overwrites dW.
 void launch_dw_gemm(DType t, const void* GT, int V, int k_len, long long ld_gt, const void* HT, int d,
                     long long ld_ht, float* dW, bool accumulate, hipStream_t s);
+// Same from G itself ([k_len][v_pad] bf16, k-major A; k_len a multiple of 64):
+// dW[V][d] (+)= G^T * H.
+void launch_dw_gemm_kmajor(const void* G, int V, int v_pad, int k_len, long long ld_g, const void* HT,
+                           int d, long long ld_ht, float* dW, bool accumulate, hipStream_t s);
 
 }  // namespace kd
