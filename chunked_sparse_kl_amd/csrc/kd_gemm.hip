@@ -28,6 +28,14 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
 
+// v_max3_f32: IEEE maxNum of three values in one instruction (fmaxf would add
+// canonicalising moves around each operand).
+__device__ inline float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 constexpr int BM = 256;
 constexpr int ROWB = KBLOCK_BYTES;  // bytes per staged row of A or B (one K block)
 
@@ -615,9 +623,19 @@ __global__ __launch_bounds__(kFusedThreads, 1) void fwd_gemm_kernel(Operand A, O
     if (lane == owner) ep.g[(long long)row * ep.K + k] = z;
   });
 
-  const int v_base = ti.tm * BM + wr * 128 + 4 * h;  // + bi*32 + 8*i + j
-  const bool full_v = (ti.tm + 1) * BM <= ep.V;
-  // --- per-token (max, sum-exp) over this wavefront's 128 vocabulary rows
+  // --- per-token (max, sum-exp) over this wavefront's 128 vocabulary rows.
+  // Only the last vocabulary tile has rows past V: they are set to -inf once
+  // (a uniform branch), so the two passes below need no per-element test.
+  if ((ti.tm + 1) * BM > ep.V) {
+    const int v_base = ti.tm * BM + wr * 128 + 4 * h;  // + bi*32 + 8*i + j
+#pragma unroll
+    for (int bj = 0; bj < NBJ; ++bj)
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (v_base + bi * 32 + 8 * (e >> 2) + (e & 3) >= ep.V) acc[bi][bj][e] = kNegInf;
+  }
   float tmax[NBJ], tsum[NBJ];
 #pragma unroll
   for (int bj = 0; bj < NBJ; ++bj) {
@@ -625,22 +643,15 @@ __global__ __launch_bounds__(kFusedThreads, 1) void fwd_gemm_kernel(Operand A, O
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int v = v_base + bi * 32 + 8 * (e >> 2) + (e & 3);
-        if (full_v || v < ep.V) mx = fmaxf(mx, acc[bi][bj][e]);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      for (int e = 0; e < 16; e += 2) mx = max3f(mx, acc[bi][bj][e], acc[bi][bj][e + 1]);
+    mx = max3f(mx, __shfl_xor(mx, 32, 64), mx);
     float sm = 0.f;
     if (mx != kNegInf) {
       const float mxs = mx * kLog2e;
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int v = v_base + bi * 32 + 8 * (e >> 2) + (e & 3);
-          const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[bi][bj][e], kLog2e, -mxs));
-          if (full_v || v < ep.V) sm += x;
-        }
+        for (int e = 0; e < 16; ++e) sm += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[bi][bj][e], kLog2e, -mxs));
     }
     sm += __shfl_xor(sm, 32, 64);
     tmax[bj] = mx;
@@ -693,7 +704,6 @@ __global__ __launch_bounds__(kFusedThreads, 1) void recompute_gemm_kernel(Operan
   const int kb_end = (k_elems + Traits<T>::BK - 1) / Traits<T>::BK;
   gemm_mainloop<T, BN, WC>(A, B, k_elems, ti.tm, ti.tn, 0, kb_end, lds, acc);
 
-  const bool full_v = (ti.tm + 1) * BM <= ep.V;
   const int nv = ep.ctrl->n_valid;
   const float gw = nv > 0 ? ep.grad_loss[0] / (float)nv : 0.f;
 #pragma unroll
@@ -707,10 +717,18 @@ __global__ __launch_bounds__(kFusedThreads, 1) void recompute_gemm_kernel(Operan
     for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int v = v_wave + bi * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
         const float q = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[bi][bj][e], kLog2e, -lse2));
-        acc[bi][bj][e] = (coef != 0.f && (full_v || v < ep.V)) ? coef * q : 0.f;
+        acc[bi][bj][e] = live ? coef * q : 0.f;
       }
+  }
+  if ((ti.tm + 1) * BM > ep.V) {  // last vocabulary tile: rows past V carry no gradient
+#pragma unroll
+    for (int bj = 0; bj < NBJ; ++bj)
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (v_wave + bi * 32 + 8 * (e >> 2) + 4 * h + (e & 3) >= ep.V) acc[bi][bj][e] = 0.f;
   }
   // Teacher entries: G -= gw * p at (t, i_{t,k}) (masked rows have none).
   wh.for_each(ep.hits, [&](int q, int owner, int, int, float p) {
