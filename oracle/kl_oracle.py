@@ -28,10 +28,20 @@ Readings of what the pages leave open (each is listed with its reason in the
 design notes of the repository):
   * no tail bucket: the student is normalised over all V, the teacher's mass
     lives only on its K ids (renormalised), the KL sums over those K ids;
-  * forward KL(teacher || student), temperature 1, mean over unmasked rows;
+  * forward KL(teacher || student), mean over unmasked rows;
   * masked rows are skipped entirely (their ids / values may be garbage);
   * duplicate ids in a row are summed in the gradient (scatter-add);
-  * a log-value of -inf is a zero-probability entry.
+  * a log-value of -inf is a zero-probability entry; an id below 0 marks a
+    padding entry (rows with fewer than K cached entries), treated the same
+    way whatever its log-value.
+
+Temperature (an extension; the pages never mention one, the default 1 is the
+method as described): the usual soft-target distillation with both sides
+softened and the loss scaled back by tau^2, i.e. steps 2-5 on z / tau and
+a / tau, loss = tau^2 * mean KL, and hence
+  G_{t,v} = gamma * tau * [mask_t] / N_valid * (S_t q_{t,v} - sum_k p_{t,k} [i_{t,k} = v])
+with q and p the softened distributions.  ``lse`` is then LSE_t(z / tau) and
+``row_kl`` is tau^2 KL_t.
 
 All arithmetic is float64; inputs are upcast exactly from their storage dtype.
 ``rows`` restricts the work to a subset of positions (for the large
@@ -106,7 +116,15 @@ def _row_blocks(rows: np.ndarray, chunk):
         yield rows[s:s + chunk]
 
 
-def forward(H, W, idx, logp, mask=None, chunk=None, rows=None) -> dict:
+def _teacher_inputs(idx: np.ndarray, a: np.ndarray, temperature: float):
+    """Padding entries (id < 0) become zero-probability entries at id 0; the
+    log-values are softened by the temperature."""
+    pad = idx < 0
+    a = np.where(pad, -np.inf, a / temperature)
+    return np.where(pad, 0, idx), a, pad
+
+
+def forward(H, W, idx, logp, mask=None, chunk=None, rows=None, temperature: float = 1.0) -> dict:
     """Loss and per-row quantities.
 
     Returns a dict with: ``loss`` (float; over the rows in ``rows`` that are
@@ -114,11 +132,13 @@ def forward(H, W, idx, logp, mask=None, chunk=None, rows=None) -> dict:
     ``lse`` [R], ``g`` [R, K] (student logits at the teacher ids; NaN, i.e.
     undefined, on masked rows, whose ids are never read), ``rows``.
     ``chunk`` processes the rows in independent blocks of that many rows.
+    With a temperature, ``lse`` is LSE(z / tau), ``row_kl`` is tau^2 KL_t and
+    ``g`` stays the raw logit z; padding entries have g = NaN.
     """
     H = to_f64(H)
     W = to_f64(W)
-    idx = np.asarray(idx)
-    a_all = to_f64(logp)
+    idx, a_all, pad = _teacher_inputs(np.asarray(idx), to_f64(logp), float(temperature))
+    tau = float(temperature)
     T = H.shape[0]
     mask = np.ones(T, dtype=np.uint8) if mask is None else np.asarray(mask)
     rows = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
@@ -128,15 +148,15 @@ def forward(H, W, idx, logp, mask=None, chunk=None, rows=None) -> dict:
     pos = 0
     for blk in _row_blocks(rows, chunk):
         z = student_logits(H[blk], W)
-        lse_b, logq = full_log_softmax(z)
+        lse_b, logq = full_log_softmax(z / tau)
         live = mask[blk] != 0
         kl = np.zeros(blk.size)
         g_b = np.full((blk.size, idx.shape[1]), np.nan)  # undefined for masked rows
         if live.any():
             ids_live = idx[blk][live]
-            g_b[live] = gather(z[live], ids_live)
+            g_b[live] = np.where(pad[blk][live], np.nan, gather(z[live], ids_live))
             l, p = renormalise_teacher(a_all[blk][live])
-            kl[live] = kl_rows(p, l, gather(logq[live], ids_live))
+            kl[live] = tau * tau * kl_rows(p, l, gather(logq[live], ids_live))
         row_kl[pos:pos + blk.size] = kl
         lse[pos:pos + blk.size] = lse_b
         g[pos:pos + blk.size] = g_b
@@ -146,7 +166,8 @@ def forward(H, W, idx, logp, mask=None, chunk=None, rows=None) -> dict:
     return {"loss": loss, "row_kl": row_kl, "lse": lse, "g": g, "rows": rows, "n_valid": nv}
 
 
-def backward(H, W, idx, logp, mask=None, grad_loss: float = 1.0, chunk=None, rows=None) -> dict:
+def backward(H, W, idx, logp, mask=None, grad_loss: float = 1.0, chunk=None, rows=None,
+             temperature: float = 1.0) -> dict:
     """dH [T, d] and dW [V, d] of ``grad_loss * loss`` (step 6).
 
     With ``rows`` given, only those rows contribute (the others are treated as
@@ -154,8 +175,8 @@ def backward(H, W, idx, logp, mask=None, grad_loss: float = 1.0, chunk=None, row
     """
     H = to_f64(H)
     W = to_f64(W)
-    idx = np.asarray(idx)
-    a_all = to_f64(logp)
+    idx, a_all, _ = _teacher_inputs(np.asarray(idx), to_f64(logp), float(temperature))
+    tau = float(temperature)
     T, d = H.shape
     V = W.shape[0]
     mask = np.ones(T, dtype=np.uint8) if mask is None else np.asarray(mask)
@@ -168,7 +189,7 @@ def backward(H, W, idx, logp, mask=None, grad_loss: float = 1.0, chunk=None, row
         return {"dH": dH, "dW": dW, "n_valid": 0}
     for blk in _row_blocks(live_rows, chunk):
         z = student_logits(H[blk], W)
-        _, logq = full_log_softmax(z)
+        _, logq = full_log_softmax(z / tau)
         q = np.exp(logq)
         _, p = renormalise_teacher(a_all[blk])
         S = p.sum(axis=1)
@@ -176,7 +197,7 @@ def backward(H, W, idx, logp, mask=None, grad_loss: float = 1.0, chunk=None, row
         scatter = np.zeros_like(G)
         r = np.repeat(np.arange(blk.size), idx.shape[1])
         np.add.at(scatter, (r, idx[blk].astype(np.int64).ravel()), p.ravel())
-        G = (grad_loss / nv) * (G - scatter)
+        G = (grad_loss * tau / nv) * (G - scatter)
         dH[blk] = G @ W
         dW += G.T @ H[blk]
     return {"dH": dH, "dW": dW, "n_valid": nv}

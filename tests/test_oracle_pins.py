@@ -288,3 +288,87 @@ def test_neg_inf_teacher_entry_is_zero_probability():
     a = O.forward(H, W, idx, lp, mask)["loss"]
     b = O.forward(H, W, idx[:, :-1], logp[:, :-1], mask)["loss"]
     assert np.isfinite(a) and abs(a - b) <= 1e-13 * b
+
+
+# ---------------------------------------------------------------- temperature and padding (extensions)
+def test_temperature_one_is_the_plain_method():
+    H, W, idx, logp, mask = _rand_case(seed=31)
+    a, b = O.forward(H, W, idx, logp, mask), O.forward(H, W, idx, logp, mask, temperature=1.0)
+    assert a["loss"] == b["loss"] and np.array_equal(a["lse"], b["lse"])
+    ga, gb = O.backward(H, W, idx, logp, mask), O.backward(H, W, idx, logp, mask, temperature=1.0)
+    assert np.array_equal(ga["dW"], gb["dW"])
+
+
+def test_temperature_scaling_identity():
+    """Scaling H, the teacher log-values and tau by c leaves both softened
+    distributions unchanged, so the tau^2-scaled loss grows by exactly c^2 (a
+    missing teacher softening or a missing tau^2 breaks this)."""
+    H, W, idx, logp, mask = _rand_case(seed=32)
+    for tau, c in ((2.0, 3.0), (0.5, 0.25)):
+        base = O.forward(H, W, idx, logp, mask, temperature=tau)
+        scaled = O.forward(c * H, W, idx, c * logp, mask, temperature=c * tau)
+        assert abs(scaled["loss"] - c * c * base["loss"]) <= 1e-12 * abs(c * c * base["loss"])
+        np.testing.assert_allclose(scaled["lse"], base["lse"], rtol=1e-12)
+
+
+def test_temperature_matches_torch_dense_softened_kl():
+    """tau^2 * KL(softmax(a/tau) || softmax(z/tau)) through torch's log_softmax / kl_div."""
+    H, W, idx, logp, mask = _rand_case(seed=33)
+    tau = 2.5
+    Ht, Wt = torch.as_tensor(H), torch.as_tensor(W)
+    logq = F.log_softmax(Ht @ Wt.T / tau, dim=1)
+    p = torch.softmax(torch.as_tensor(logp) / tau, dim=1)
+    m = torch.as_tensor(mask != 0)
+    P = torch.zeros_like(logq).scatter_add_(1, torch.as_tensor(idx, dtype=torch.int64), p)
+    ref = (tau * tau * F.kl_div(logq[m], P[m], reduction="sum") / m.sum()).item()
+    assert abs(O.forward(H, W, idx, logp, mask, temperature=tau)["loss"] - ref) <= 1e-12 * abs(ref)
+
+
+@pytest.mark.parametrize("tau", [2.0, 0.6])
+def test_temperature_gradients_finite_differences(tau):
+    H, W, idx, logp, mask = _rand_case(T=5, d=6, V=24, K=4, masked=1, seed=34)
+    bw = O.backward(H, W, idx, logp, mask, grad_loss=1.3, temperature=tau)
+    eps = 1e-6
+
+    def L(Hx, Wx):
+        return 1.3 * O.forward(Hx, Wx, idx, logp, mask, temperature=tau)["loss"]
+
+    num_dH = np.zeros_like(H)
+    for i in range(H.shape[0]):
+        for j in range(H.shape[1]):
+            Hp, Hm = H.copy(), H.copy()
+            Hp[i, j] += eps
+            Hm[i, j] -= eps
+            num_dH[i, j] = (L(Hp, W) - L(Hm, W)) / (2 * eps)
+    num_dW = np.zeros_like(W)
+    for i in range(W.shape[0]):
+        for j in range(W.shape[1]):
+            Wp, Wm = W.copy(), W.copy()
+            Wp[i, j] += eps
+            Wm[i, j] -= eps
+            num_dW[i, j] = (L(H, Wp) - L(H, Wm)) / (2 * eps)
+    rel = lambda a, b: np.linalg.norm(a - b) / np.linalg.norm(b)
+    assert rel(bw["dH"], num_dH) <= 1e-6
+    assert rel(bw["dW"], num_dW) <= 1e-6
+
+
+def test_padding_entries_equal_zero_probability_entries():
+    """An id below 0 is a padding entry: the same as a valid id with log-value
+    -inf, whatever log-value the padding carries."""
+    H, W, idx, logp, mask = _rand_case(seed=35)
+    pad_idx, pad_logp = idx.copy(), logp.copy()
+    pad_idx[2, 3:] = -1
+    pad_idx[5, 0] = -7
+    pad_logp[2, 3:] = 1e3          # garbage under the padding
+    ref_logp = logp.copy()
+    ref_logp[2, 3:] = -np.inf
+    ref_logp[5, 0] = -np.inf
+    for tau in (1.0, 1.7):
+        a = O.forward(H, W, pad_idx, pad_logp, mask, temperature=tau)
+        b = O.forward(H, W, idx, ref_logp, mask, temperature=tau)
+        assert abs(a["loss"] - b["loss"]) <= 1e-13 * abs(b["loss"])
+        assert np.isnan(a["g"][2, 3:]).all() and np.isnan(a["g"][5, 0])
+        ga = O.backward(H, W, pad_idx, pad_logp, mask, temperature=tau)
+        gb = O.backward(H, W, idx, ref_logp, mask, temperature=tau)
+        np.testing.assert_allclose(ga["dW"], gb["dW"], rtol=1e-12, atol=1e-16)
+        np.testing.assert_allclose(ga["dH"], gb["dH"], rtol=1e-12, atol=1e-16)
