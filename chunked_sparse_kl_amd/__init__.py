@@ -68,11 +68,12 @@ def _load():
     lib = ctypes.CDLL(path)
     vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
     lib.kd_plan_query.argtypes = [ctypes.c_int, i64, i64, i64, i32, i64, sz, ctypes.POINTER(KdPlan)]
+    f32 = ctypes.c_float
     lib.kd_fused_chunked_kl_fwd.argtypes = [
-        ctypes.c_int, vp, vp, vp, vp, vp, i64, i64, i64, i32, i64, vp, sz, vp, vp, vp, vp, vp]
+        ctypes.c_int, vp, vp, vp, vp, vp, i64, i64, i64, i32, i64, f32, vp, sz, vp, vp, vp, vp, vp]
     lib.kd_fused_chunked_kl_bwd.argtypes = [
-        ctypes.c_int, vp, vp, vp, vp, vp, i64, i64, i64, i32, i64, vp, vp, vp, vp, ctypes.c_int, vp, sz,
-        vp]
+        ctypes.c_int, vp, vp, vp, vp, vp, i64, i64, i64, i32, i64, f32, vp, vp, vp, vp, ctypes.c_int,
+        vp, sz, vp]
     lib.kd_status_string.argtypes = [ctypes.c_int]
     lib.kd_status_string.restype = ctypes.c_char_p
     lib.kd_last_error_message.argtypes = []
@@ -159,9 +160,11 @@ def _workspace(nbytes: int, device, workspace):
 
 
 def kd_fused_chunked_kl_fwd(H, W, topk_idx, topk_logp, mask=None, chunk: int = 0, workspace=None,
-                            row_kl: bool = True, gathered: bool = False, plan: dict | None = None):
+                            row_kl: bool = True, gathered: bool = False, plan: dict | None = None,
+                            temperature: float = 1.0):
     """Forward call.  Returns a dict with loss [1], lse [n], row_kl [n] (optional),
-    gathered [n, K] (optional) and the plan used."""
+    gathered [n, K] (optional) and the plan used.  ``temperature`` softens both
+    sides and scales the loss by its square; ids < 0 in ``topk_idx`` are padding."""
     n, d, V, K = _check_inputs(H, W, topk_idx, topk_logp, mask)
     dt = _dtype_code(H)
     plan = plan or kd_plan_query(dt, n, d, V, K, chunk)
@@ -172,16 +175,17 @@ def kd_fused_chunked_kl_fwd(H, W, topk_idx, topk_logp, mask=None, chunk: int = 0
     g = torch.empty((n, K), dtype=torch.float32, device=H.device) if gathered else None
     _check(lib().kd_fused_chunked_kl_fwd(
         dt, _ptr(H), _ptr(W), _ptr(topk_idx), _ptr(topk_logp), _ptr(mask), n, d, V, K,
-        plan["chunk"], _ptr(ws), ws.numel() * ws.element_size(), _ptr(loss), _ptr(lse), _ptr(rk),
-        _ptr(g), _stream(H.device)))
+        plan["chunk"], float(temperature), _ptr(ws), ws.numel() * ws.element_size(), _ptr(loss),
+        _ptr(lse), _ptr(rk), _ptr(g), _stream(H.device)))
     return {"loss": loss, "lse": lse, "row_kl": rk, "gathered": g, "plan": plan}
 
 
 def kd_fused_chunked_kl_bwd(H, W, topk_idx, topk_logp, mask, lse, grad_loss=None, chunk: int = 0,
-                            workspace=None, dW=None, plan: dict | None = None, accumulate: bool = True):
+                            workspace=None, dW=None, plan: dict | None = None, accumulate: bool = True,
+                            temperature: float = 1.0):
     """Backward call.  Returns (dH, dW).  A given dW is accumulated into
     (accumulate=True) or overwritten (accumulate=False); without one, a new
-    dW is allocated and written."""
+    dW is allocated and written.  ``temperature`` must be the forward call's."""
     n, d, V, K = _check_inputs(H, W, topk_idx, topk_logp, mask)
     dt = _dtype_code(H)
     plan = plan or kd_plan_query(dt, n, d, V, K, chunk)
@@ -197,7 +201,8 @@ def kd_fused_chunked_kl_bwd(H, W, topk_idx, topk_logp, mask, lse, grad_loss=None
         raise ValueError("dW must be a contiguous float32 [V, d] tensor")
     _check(lib().kd_fused_chunked_kl_bwd(
         dt, _ptr(H), _ptr(W), _ptr(topk_idx), _ptr(topk_logp), _ptr(mask), n, d, V, K,
-        plan["chunk"], _ptr(lse), _ptr(grad_loss), _ptr(dH), _ptr(dW), 1 if accumulate else 0,
+        plan["chunk"], float(temperature), _ptr(lse), _ptr(grad_loss), _ptr(dH), _ptr(dW),
+        1 if accumulate else 0,
         _ptr(ws), ws.numel() * ws.element_size(), _stream(H.device)))
     return dH, dW
 
@@ -224,21 +229,25 @@ def kd_profile_read() -> list[dict]:
 
 class _FusedChunkedKL(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, H, W, topk_idx, topk_logp, mask, chunk):
-        out = kd_fused_chunked_kl_fwd(H, W, topk_idx, topk_logp, mask, chunk, row_kl=False)
+    def forward(ctx, H, W, topk_idx, topk_logp, mask, chunk, temperature):
+        out = kd_fused_chunked_kl_fwd(H, W, topk_idx, topk_logp, mask, chunk, row_kl=False,
+                                      temperature=temperature)
         ctx.save_for_backward(H, W, topk_idx, topk_logp, mask, out["lse"])
         ctx.plan = out["plan"]
+        ctx.temperature = temperature
         return out["loss"][0]
 
     @staticmethod
     def backward(ctx, grad):
         H, W, topk_idx, topk_logp, mask, lse = ctx.saved_tensors
         dH, dW = kd_fused_chunked_kl_bwd(H, W, topk_idx, topk_logp, mask, lse,
-                                         grad.reshape(1), plan=ctx.plan)
-        return dH, dW.to(W.dtype), None, None, None, None
+                                         grad.reshape(1), plan=ctx.plan,
+                                         temperature=ctx.temperature)
+        return dH, dW.to(W.dtype), None, None, None, None, None
 
 
-def fused_chunked_kl(H, W, topk_idx, topk_logp, mask=None, chunk: int = 0):
+def fused_chunked_kl(H, W, topk_idx, topk_logp, mask=None, chunk: int = 0, temperature: float = 1.0):
     """Mean KL(teacher top-K renormalised || student full softmax) over unmasked rows,
-    differentiable w.r.t. H and W."""
-    return _FusedChunkedKL.apply(H, W, topk_idx, topk_logp, mask, chunk)
+    differentiable w.r.t. H and W.  With a temperature tau both distributions
+    are softened by it and the loss is multiplied by tau^2."""
+    return _FusedChunkedKL.apply(H, W, topk_idx, topk_logp, mask, chunk, float(temperature))

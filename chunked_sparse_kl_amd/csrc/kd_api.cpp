@@ -302,15 +302,24 @@ int check_common(const void* H, const void* W, const int32_t* idx, const float* 
   return KD_OK;
 }
 
+// The temperature divides both sides' log-values, so it must be a positive
+// finite number.
+int check_temperature(float tau) {
+  if (!(tau > 0.f) || !std::isfinite(tau))
+    return fail(KD_E_INVAL, "temperature %g must be positive and finite", (double)tau);
+  return KD_OK;
+}
+
 // Teacher preparation and bucketing shared by both calls.
 int prepare_teacher(const Layout& L, const int32_t* idx, const float* logp, const uint8_t* mask,
-                    char* ws, hipStream_t s) {
+                    float tau, char* ws, hipStream_t s) {
   auto* ctrl = reinterpret_cast<kd::Ctrl*>(ws + L.ctrl);
   const int n = (int)L.n, K = (int)L.K, V = (int)L.V;
   const double nk = double(L.n) * L.K;
   KD_LAUNCH("fill", 0, 0, kd::launch_fill_i32(reinterpret_cast<int*>(ctrl), 64, 0, s));
   KD_LAUNCH("teacher_bucket", 0, nk * 32 + L.n * 9.0,
-            kd::launch_teacher_bucket(logp, idx, mask, n, K, V, reinterpret_cast<float*>(ws + L.p),
+            kd::launch_teacher_bucket(logp, idx, mask, n, K, V, 1.0f / tau,
+                                      reinterpret_cast<float*>(ws + L.p),
                                       reinterpret_cast<float*>(ws + L.S),
                                       reinterpret_cast<float*>(ws + L.E),
                                       reinterpret_cast<int*>(ws + L.hit_off),
@@ -321,7 +330,7 @@ int prepare_teacher(const Layout& L, const int32_t* idx, const float* logp, cons
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return fail(KD_E_HIP, "validation read-back: %s", hipGetErrorString(e));
     if (host.range_error)
-      return fail(KD_E_RANGE, "an unmasked row holds a teacher id outside [0, %d)", V);
+      return fail(KD_E_RANGE, "an unmasked row holds a teacher id >= V = %d", V);
   }
   return KD_OK;
 }
@@ -392,9 +401,9 @@ int kd_plan_query(int dtype, int64_t n, int64_t d, int64_t V, int32_t K, int64_t
 
 int kd_fused_chunked_kl_fwd(int dtype, const void* H, const void* W, const int32_t* topk_idx,
                             const float* topk_logp, const uint8_t* mask, int64_t n, int64_t d,
-                            int64_t V, int32_t K, int64_t chunk, void* workspace,
-                            size_t workspace_bytes, float* loss, float* lse, float* row_kl,
-                            float* gathered, void* stream) {
+                            int64_t V, int32_t K, int64_t chunk, float temperature,
+                            void* workspace, size_t workspace_bytes, float* loss, float* lse,
+                            float* row_kl, float* gathered, void* stream) {
   Layout L;
   int rc = plan(dtype, n, d, V, K, chunk, workspace_bytes ? workspace_bytes : 1, &L);
   if (rc != KD_OK && rc != KD_E_WORKSPACE) return rc;
@@ -403,11 +412,13 @@ int kd_fused_chunked_kl_fwd(int dtype, const void* H, const void* W, const int32
     return rc;
   }
   if (loss == nullptr || lse == nullptr) return fail(KD_E_INVAL, "loss and lse must be non-null");
+  rc = check_temperature(temperature);
+  if (rc != KD_OK) return rc;
   rc = check_common(H, W, topk_idx, topk_logp, workspace, workspace_bytes, L.fwd_end);
   if (rc != KD_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  rc = prepare_teacher(L, topk_idx, topk_logp, mask, ws, s);
+  rc = prepare_teacher(L, topk_idx, topk_logp, mask, temperature, ws, s);
   if (rc != KD_OK) return rc;
 
   const size_t es = kd::elem_size(L.dt);
@@ -428,6 +439,7 @@ int kd_fused_chunked_kl_fwd(int dtype, const void* H, const void* W, const int32
     ep.hit_off = reinterpret_cast<const int*>(ws + L.hit_off);
     ep.hits = reinterpret_cast<const kd::Hit*>(ws + L.hits);
     ep.g = g;
+    ep.inv_tau = 1.0f / temperature;
     const char* Hc = static_cast<const char*>(H) + c0 * L.d * es;
     const double fl = 2.0 * rows * L.d * L.V;
     const double by = double(L.V) * L.d * es + double(rows) * L.d * es + double(rows) * L.n_vt * 8;
@@ -436,7 +448,8 @@ int kd_fused_chunked_kl_fwd(int dtype, const void* H, const void* W, const int32
               kd::launch_lse_kl(part, (int)L.chunk, (int)L.n_vt, (int)c0, rows,
                                 reinterpret_cast<const float*>(ws + L.p), g,
                                 reinterpret_cast<const float*>(ws + L.S),
-                                reinterpret_cast<const float*>(ws + L.E), mask, (int)L.K, lse, rk, s));
+                                reinterpret_cast<const float*>(ws + L.E), mask, (int)L.K,
+                                temperature, lse, rk, s));
   }
   KD_LAUNCH("loss", 0, L.n * 4.0,
             kd::launch_loss(rk, (int)L.n, reinterpret_cast<const kd::Ctrl*>(ws + L.ctrl), loss, s));
@@ -445,8 +458,9 @@ int kd_fused_chunked_kl_fwd(int dtype, const void* H, const void* W, const int32
 
 int kd_fused_chunked_kl_bwd(int dtype, const void* H, const void* W, const int32_t* topk_idx,
                             const float* topk_logp, const uint8_t* mask, int64_t n, int64_t d,
-                            int64_t V, int32_t K, int64_t chunk, const float* lse,
-                            const float* grad_loss, void* dH, float* dW, int accumulate_dw,
+                            int64_t V, int32_t K, int64_t chunk, float temperature,
+                            const float* lse, const float* grad_loss, void* dH, float* dW,
+                            int accumulate_dw,
                             void* workspace, size_t workspace_bytes, void* stream) {
   Layout L;
   int rc = plan(dtype, n, d, V, K, chunk, workspace_bytes ? workspace_bytes : 1, &L);
@@ -454,11 +468,13 @@ int kd_fused_chunked_kl_bwd(int dtype, const void* H, const void* W, const int32
   if (lse == nullptr || grad_loss == nullptr || dH == nullptr || dW == nullptr)
     return fail(KD_E_INVAL, "lse, grad_loss, dH and dW must be non-null");
   if (!aligned16(dH) || !aligned16(dW)) return fail(KD_E_INVAL, "dH and dW must be 16-byte aligned");
+  rc = check_temperature(temperature);
+  if (rc != KD_OK) return rc;
   rc = check_common(H, W, topk_idx, topk_logp, workspace, workspace_bytes, L.bwd_end);
   if (rc != KD_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  rc = prepare_teacher(L, topk_idx, topk_logp, mask, ws, s);
+  rc = prepare_teacher(L, topk_idx, topk_logp, mask, temperature, ws, s);
   if (rc != KD_OK) return rc;
 
   const size_t es = kd::elem_size(L.dt);
@@ -498,6 +514,8 @@ int kd_fused_chunked_kl_bwd(int dtype, const void* H, const void* W, const int32
     ep.mask = mask;
     ep.ctrl = reinterpret_cast<const kd::Ctrl*>(ws + L.ctrl);
     ep.grad_loss = grad_loss;
+    ep.tau = temperature;
+    ep.inv_tau = 1.0f / temperature;
     const double fl = 2.0 * rows * L.d * L.V;
     KD_LAUNCH("recompute_gemm", fl,
               double(L.V) * L.d * es + double(rows) * L.d * es + 2.0 * c_pad * L.v_pad * es,

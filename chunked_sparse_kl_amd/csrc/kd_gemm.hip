@@ -597,9 +597,10 @@ struct WaveHits {
 };
 
 // ------------------------------------------------------------------ forward
-// D[v][t] = z_{t,v}.  Per token: max and sum of exp(z - max) over this tile's
-// vocabulary rows (-> one (max, sum) partial per vocabulary tile); the logits
-// at the token's teacher ids are read straight out of the accumulators.
+// D[v][t] = z_{t,v}.  Per token: max and sum of exp(z/tau - max) over this
+// tile's vocabulary rows (-> one (max, sum) partial of the softened logits per
+// vocabulary tile; tau > 0, so max(z/tau) = max(z)/tau); the raw logits at the
+// token's teacher ids are read straight out of the accumulators.
 template <typename T>
 __global__ __launch_bounds__(kFusedThreads, 1) void fwd_gemm_kernel(Operand A, Operand B, int k_elems,
                                                                      int tiles_m, int tiles_n,
@@ -646,15 +647,16 @@ __global__ __launch_bounds__(kFusedThreads, 1) void fwd_gemm_kernel(Operand A, O
       for (int e = 0; e < 16; e += 2) mx = max3f(mx, acc[bi][bj][e], acc[bi][bj][e + 1]);
     mx = max3f(mx, __shfl_xor(mx, 32, 64), mx);
     float sm = 0.f;
+    const float sc = kLog2e * ep.inv_tau;
     if (mx != kNegInf) {
-      const float mxs = mx * kLog2e;
+      const float mxs = mx * sc;
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sm += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[bi][bj][e], kLog2e, -mxs));
+        for (int e = 0; e < 16; ++e) sm += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[bi][bj][e], sc, -mxs));
     }
     sm += __shfl_xor(sm, 32, 64);
-    tmax[bj] = mx;
+    tmax[bj] = mx * ep.inv_tau;
     tsum[bj] = sm;
   }
   // --- merge the two vocabulary halves (wr = 0, 1) through LDS
@@ -680,7 +682,8 @@ __global__ __launch_bounds__(kFusedThreads, 1) void fwd_gemm_kernel(Operand A, O
 
 // ------------------------------------------------------------------ recompute
 // D[v][t] = z_{t,v} again; G_{t,v} = gw*S_t*q_{t,v} - gw*sum_k p_{t,k}[i_{t,k} = v]
-// with gw = grad_loss * mask_t / N_valid, formed in the accumulators (the
+// with q = softmax(z / tau) and gw = tau * grad_loss * mask_t / N_valid (the
+// derivative of tau^2 KL through z / tau), formed in the accumulators (the
 // scatter goes straight into the owning registers), rounded to T and written
 // transposed (G^T, straight from registers: a lane's 32-token column is
 // contiguous there) and row-major (G, through a per-wavefront LDS block so the
@@ -705,7 +708,8 @@ __global__ __launch_bounds__(kFusedThreads, 1) void recompute_gemm_kernel(Operan
   gemm_mainloop<T, BN, WC>(A, B, k_elems, ti.tm, ti.tn, 0, kb_end, lds, acc);
 
   const int nv = ep.ctrl->n_valid;
-  const float gw = nv > 0 ? ep.grad_loss[0] / (float)nv : 0.f;
+  const float gw = nv > 0 ? ep.tau * ep.grad_loss[0] / (float)nv : 0.f;
+  const float sc = kLog2e * ep.inv_tau;
 #pragma unroll
   for (int bj = 0; bj < NBJ; ++bj) {
     const int n = n_wave + bj * 32 + r32;
@@ -717,7 +721,7 @@ __global__ __launch_bounds__(kFusedThreads, 1) void recompute_gemm_kernel(Operan
     for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float q = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[bi][bj][e], kLog2e, -lse2));
+        const float q = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[bi][bj][e], sc, -lse2));
         acc[bi][bj][e] = live ? coef * q : 0.f;
       }
   }

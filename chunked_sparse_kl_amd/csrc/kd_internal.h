@@ -50,11 +50,11 @@ void launch_fill_i32(int* p, long long count, int value, hipStream_t s);
 // row block rb owns the hit range [rb * 64 * K, (rb + 1) * 64 * K).
 constexpr int kMaxVocabTiles = 16383;  // LDS bucket counters of one workgroup (64 KB)
 void launch_teacher_bucket(const float* logp, const int* idx, const uint8_t* mask, int n, int K,
-                           int V, float* p, float* S, float* E, int* hit_off, Hit* hits,
-                           Ctrl* ctrl, hipStream_t s);
+                           int V, float inv_tau, float* p, float* S, float* E, int* hit_off,
+                           Hit* hits, Ctrl* ctrl, hipStream_t s);
 void launch_lse_kl(const float2* part, int ld_part, int n_vt, int c0, int rows, const float* p,
                    const float* g, const float* S, const float* E, const uint8_t* mask, int K,
-                   float* lse, float* row_kl, hipStream_t s);
+                   float tau, float* lse, float* row_kl, hipStream_t s);
 void launch_loss(const float* row_kl, int n, const Ctrl* ctrl, float* loss, hipStream_t s);
 void launch_transpose_pad(DType t, const void* in, int rows, int cols, long long ld_in, void* out,
                           int rows_pad, long long ld_out, hipStream_t s);
@@ -74,6 +74,7 @@ struct FwdEpilogue {
   const int* hit_off;  // [n_rb][n_vt + 1]
   const Hit* hits;     // bucketed by (row block, vocab tile)
   float* g;            // [n, K] gathered logits
+  float inv_tau;       // 1 / temperature: the statistics are over z / tau
 };
 
 struct RecomputeEpilogue {
@@ -96,6 +97,8 @@ struct RecomputeEpilogue {
   const uint8_t* mask; // [n] or null
   const Ctrl* ctrl;
   const float* grad_loss;
+  float tau;           // temperature: q = softmax(z / tau), G carries a factor tau
+  float inv_tau;
 };
 
 // Z = W * H_c^T over one chunk (vocab rows x chunk tokens), epilogue: per

@@ -62,10 +62,12 @@ __device__ inline int block256_exclusive_scan(int v, int* sh, int* total) {
 // E = sum p*l (0*log 0 := 0), and counts the row's ids per vocabulary tile in
 // LDS.  The counts are then scanned into this block's bucket offsets and every
 // entry is placed in its bucket with LDS cursors.  Masked rows are skipped
-// entirely; ids outside [0, V) set the range flag and are dropped.
+// entirely; ids >= V set the range flag and are dropped; ids < 0 are padding
+// (probability 0, outside the renormalisation).  The log-values are divided
+// by the temperature (inv_tau = 1 / tau) before the renormalisation.
 __global__ __launch_bounds__(256) void teacher_bucket_kernel(
     const float* __restrict__ logp, const int* __restrict__ idx, const uint8_t* __restrict__ mask,
-    int n, int K, int V, int n_vt, float* __restrict__ p, float* __restrict__ S,
+    int n, int K, int V, int n_vt, float inv_tau, float* __restrict__ p, float* __restrict__ S,
     float* __restrict__ E, int* __restrict__ hit_off, Hit* __restrict__ hits, Ctrl* ctrl) {
   extern __shared__ int cnt[];  // n_vt + 1 counters, then cursors
   __shared__ int sh[4];
@@ -89,16 +91,18 @@ __global__ __launch_bounds__(256) void teacher_bucket_kernel(
       continue;
     }
     ++live_rows;
+    // softened log-value of entry k; padding entries (id < 0) count as -inf
+    auto a_of = [&](int k) { return idx[base + k] < 0 ? kNegInf : logp[base + k] * inv_tau; };
     float mx = kNegInf;
-    for (int k = lane; k < K; k += 64) mx = fmaxf(mx, logp[base + k]);
+    for (int k = lane; k < K; k += 64) mx = fmaxf(mx, a_of(k));
     mx = wave_max(mx);
     float se = 0.f;
-    for (int k = lane; k < K; k += 64) se += expf(logp[base + k] - mx);
+    for (int k = lane; k < K; k += 64) se += expf(a_of(k) - mx);
     se = wave_sum(se);
     const float lam = mx + logf(se);
     float sp = 0.f, e = 0.f;
     for (int k = lane; k < K; k += 64) {
-      const float l = logp[base + k] - lam;
+      const float l = a_of(k) - lam;
       const float pk = expf(l);
       p[base + k] = pk;
       sp += pk;
@@ -106,7 +110,7 @@ __global__ __launch_bounds__(256) void teacher_bucket_kernel(
       const int v = idx[base + k];
       if (v >= 0 && v < V)
         atomicAdd(&cnt[v / TILE_V], 1);
-      else
+      else if (v >= V)
         bad = true;
     }
     sp = wave_sum(sp);
@@ -161,7 +165,9 @@ __global__ __launch_bounds__(256) void teacher_bucket_kernel(
 // per-vocabulary-tile (max, sum-exp) partials j = s, s+8, ... and the teacher
 // terms k = s, s+8, ...; the slices are then combined in slice order.  The
 // merge order depends only on the number of vocabulary tiles, so LSE and KL do
-// not depend on the chunk size.  KL_t = E_t - sum_k p_k g_k + S_t * LSE_t.
+// not depend on the chunk size.  The partials are of the softened logits
+// z / tau, so LSE_t is that of z / tau, and
+// KL_t = tau^2 (E_t - sum_k p_k g_k / tau + S_t * LSE_t).
 constexpr int kKlRows = 32, kKlSlices = 8;
 __global__ __launch_bounds__(256) void lse_kl_kernel(const float2* __restrict__ part, int ld_part,
                                                      int n_vt, int c0, int rows,
@@ -170,7 +176,7 @@ __global__ __launch_bounds__(256) void lse_kl_kernel(const float2* __restrict__ 
                                                      const float* __restrict__ S,
                                                      const float* __restrict__ E,
                                                      const uint8_t* __restrict__ mask, int K,
-                                                     float* __restrict__ lse,
+                                                     float tau, float* __restrict__ lse,
                                                      float* __restrict__ row_kl) {
   __shared__ float2 red[kKlSlices][kKlRows];
   __shared__ float dred[kKlSlices][kKlRows];
@@ -215,7 +221,7 @@ __global__ __launch_bounds__(256) void lse_kl_kernel(const float2* __restrict__ 
     }
     const float L = m.x + logf(m.y);
     lse[t] = L;
-    row_kl[t] = live ? E[t] - dsum + S[t] * L : 0.f;
+    row_kl[t] = live ? tau * tau * (E[t] - dsum / tau + S[t] * L) : 0.f;
   }
 }
 
@@ -333,20 +339,20 @@ void launch_fill_i32(int* p, long long count, int value, hipStream_t s) {
 }
 
 void launch_teacher_bucket(const float* logp, const int* idx, const uint8_t* mask, int n, int K,
-                           int V, float* p, float* S, float* E, int* hit_off, Hit* hits,
-                           Ctrl* ctrl, hipStream_t s) {
+                           int V, float inv_tau, float* p, float* S, float* E, int* hit_off,
+                           Hit* hits, Ctrl* ctrl, hipStream_t s) {
   const int n_vt = (V + TILE_V - 1) / TILE_V;
   const int n_rb = (n + ROW_BLOCK - 1) / ROW_BLOCK;
   const size_t lds = size_t(n_vt + 1) * sizeof(int);
-  teacher_bucket_kernel<<<n_rb, 256, lds, s>>>(logp, idx, mask, n, K, V, n_vt, p, S, E, hit_off,
-                                               hits, ctrl);
+  teacher_bucket_kernel<<<n_rb, 256, lds, s>>>(logp, idx, mask, n, K, V, n_vt, inv_tau, p, S, E,
+                                               hit_off, hits, ctrl);
 }
 
 void launch_lse_kl(const float2* part, int ld_part, int n_vt, int c0, int rows, const float* p,
                    const float* g, const float* S, const float* E, const uint8_t* mask, int K,
-                   float* lse, float* row_kl, hipStream_t s) {
+                   float tau, float* lse, float* row_kl, hipStream_t s) {
   lse_kl_kernel<<<(rows + kKlRows - 1) / kKlRows, 256, 0, s>>>(part, ld_part, n_vt, c0, rows, p, g,
-                                                                S, E, mask, K, lse, row_kl);
+                                                                S, E, mask, K, tau, lse, row_kl);
 }
 
 void launch_loss(const float* row_kl, int n, const Ctrl* ctrl, float* loss, hipStream_t s) {

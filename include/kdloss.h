@@ -21,12 +21,14 @@
  * and its gradient (the closed form the blog refers to in its closing
  * paragraph):  G_{t,v} = grad_loss * [mask_t] / N_valid * (S_t q_{t,v} -
  * sum_k p_{t,k} [i_{t,k} = v]),  S_t = sum_k p_{t,k};  dH = G W,  dW += G^T H.
- * No tail bucket: the teacher's mass lives only on its K ids; temperature 1.
+ * No tail bucket: the teacher's mass lives only on its K ids.  At temperature
+ * 1 this is the method as the blog describes it; a temperature and padding
+ * entries are extensions, documented before the forward call.
  *
  * Layouts (all row-major, contiguous):
  *   H        [n, d]  dtype (bf16 or fp32)        student hidden states
  *   W        [V, d]  dtype                       output-projection weight
- *   topk_idx [n, K]  int32 in [0, V)             teacher ids (duplicates allowed: summed)
+ *   topk_idx [n, K]  int32 < V                   teacher ids (< 0: padding; duplicates summed)
  *   topk_logp[n, K]  fp32                        teacher log-values (any per-row offset;
  *                                                -inf = zero probability)
  *   mask     [n]     uint8, NULL = all ones      0 removes the row entirely (its ids
@@ -87,21 +89,33 @@ int kd_plan_query(int dtype, int64_t n, int64_t d, int64_t V, int32_t K, int64_t
                   size_t hbm_budget, kd_plan_t* out);
 
 /*
+ * Teacher entries and temperature (both calls):
+ *   topk_idx  [n, K] int32: vocabulary ids; an id < 0 marks a padding entry
+ *             (rows with fewer than K cached entries): it has probability 0
+ *             and is excluded from the renormalisation, whatever its log-value;
+ *             an unmasked row needs at least one id >= 0 (an all-padding row
+ *             has no teacher distribution: its results are NaN, so mask it)
+ *   temperature > 0 (finite): the student logits and the teacher log-values
+ *             are both divided by it and the loss is multiplied by its
+ *             square (soft-target distillation); 1 is the method as described.
+ *             Backward must get the same value as forward.
+ *
  * Forward: loss, per-row log-sum-exp and per-row KL.
  *   loss     [1] fp32 device, written (mean KL over unmasked rows)
  *   lse      [n] fp32 device, written: LSE over the full vocabulary of each
- *            row's logits (also for masked rows); pass it unchanged to bwd
- *   row_kl   [n] fp32 device or NULL: KL_t (0 for masked rows)
- *   gathered [n, K] fp32 device or NULL: z_{t, i_{t,k}}, the student logit at
- *            each teacher id, taken from the same GEMM tiles that feed the
- *            log-sum-exp (undefined on masked rows)
+ *            row's logits divided by the temperature (also for masked rows);
+ *            pass it unchanged to bwd
+ *   row_kl   [n] fp32 device or NULL: temperature^2 * KL_t (0 for masked rows)
+ *   gathered [n, K] fp32 device or NULL: z_{t, i_{t,k}}, the raw student logit
+ *            at each teacher id, taken from the same GEMM tiles that feed the
+ *            log-sum-exp (undefined on masked rows and padding entries)
  *   workspace: device buffer of at least plan.fwd_workspace_bytes for the same
  *            (dtype, n, d, V, K, chunk); its contents need not be initialised.
  * The result does not depend on the chunk size (bitwise, for loss and lse).
  */
 int kd_fused_chunked_kl_fwd(int dtype, const void* H, const void* W, const int32_t* topk_idx,
                             const float* topk_logp, const uint8_t* mask, int64_t n, int64_t d,
-                            int64_t V, int32_t K, int64_t chunk, void* workspace,
+                            int64_t V, int32_t K, int64_t chunk, float temperature, void* workspace,
                             size_t workspace_bytes, float* loss, float* lse, float* row_kl,
                             float* gathered, void* stream);
 
@@ -120,7 +134,7 @@ int kd_fused_chunked_kl_fwd(int dtype, const void* H, const void* W, const int32
  */
 int kd_fused_chunked_kl_bwd(int dtype, const void* H, const void* W, const int32_t* topk_idx,
                             const float* topk_logp, const uint8_t* mask, int64_t n, int64_t d,
-                            int64_t V, int32_t K, int64_t chunk, const float* lse,
+                            int64_t V, int32_t K, int64_t chunk, float temperature, const float* lse,
                             const float* grad_loss, void* dH, float* dW, int accumulate_dw,
                             void* workspace, size_t workspace_bytes, void* stream);
 

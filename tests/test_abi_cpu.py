@@ -103,14 +103,26 @@ def test_bad_sizes_rejected(kwargs, code):
 def test_null_pointers_rejected_without_device_work():
     lib = kd.lib()
     loss = ctypes.c_void_p(16)
-    rc = lib.kd_fused_chunked_kl_fwd(0, None, None, None, None, None, 256, 256, 4096, 16, 64, None, 0,
-                                     loss, loss, None, None, None)
+    rc = lib.kd_fused_chunked_kl_fwd(0, None, None, None, None, None, 256, 256, 4096, 16, 64, 1.0, None,
+                                     0, loss, loss, None, None, None)
     assert rc == -1 and b"non-null" in lib.kd_last_error_message()
     fake = ctypes.c_void_p(4096)
-    rc = lib.kd_fused_chunked_kl_fwd(0, fake, fake, fake, fake, None, 256, 256, 4096, 16, 64, None, 0,
-                                     fake, fake, None, None, None)
+    rc = lib.kd_fused_chunked_kl_fwd(0, fake, fake, fake, fake, None, 256, 256, 4096, 16, 64, 1.0, None,
+                                     0, fake, fake, None, None, None)
     assert rc == -2 and b"workspace" in lib.kd_last_error_message()
     misaligned = ctypes.c_void_p(4104)
     rc = lib.kd_fused_chunked_kl_bwd(0, misaligned, fake, fake, fake, None, 256, 256, 4096, 16, 64,
-                                     fake, fake, fake, fake, 1, fake, 1 << 30, None)
+                                     1.0, fake, fake, fake, fake, 1, fake, 1 << 30, None)
     assert rc == -1 and b"aligned" in lib.kd_last_error_message()
+
+
+@pytest.mark.parametrize("tau", [0.0, -1.0, float("nan"), float("inf")])
+def test_bad_temperature_rejected_without_device_work(tau):
+    lib = kd.lib()
+    fake = ctypes.c_void_p(4096)
+    rc = lib.kd_fused_chunked_kl_fwd(0, fake, fake, fake, fake, None, 256, 256, 4096, 16, 64, tau, fake,
+                                     1 << 30, fake, fake, None, None, None)
+    assert rc == -1 and b"temperature" in lib.kd_last_error_message()
+    rc = lib.kd_fused_chunked_kl_bwd(0, fake, fake, fake, fake, None, 256, 256, 4096, 16, 64, tau, fake,
+                                     fake, fake, fake, 1, fake, 1 << 30, None)
+    assert rc == -1 and b"temperature" in lib.kd_last_error_message()

@@ -76,6 +76,53 @@ def test_clustered_ids_overflow_tiles():
     check_full(inp, run_gpu(inp, chunk=128), "bf16")
 
 
+# ------------------------------------------------------------------ temperature, padding
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("tau", [2.0, 0.5])
+def test_temperature(dtype, tau):
+    inp = synth.make_custom(600, 192, 1100, 24, dtype, "random5", "uniform", seed=21)
+    inp["logp"] += torch.randn(600, 1) * 3.0       # any per-row offset
+    gpu = run_gpu(inp, chunk=256, grad=0.8, temperature=tau)
+    check_full(inp, gpu, dtype, grad=0.8, temperature=tau)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_padding_entries(dtype):
+    inp = synth.make_custom(500, 128, 900, 16, dtype, "random5", "uniform", seed=22)
+    rng = np.random.default_rng(22)
+    n_real = rng.integers(1, 17, size=500)         # rows hold 1..16 real entries, the rest padding
+    idx = inp["idx"].numpy()
+    for t in range(500):
+        idx[t, n_real[t]:] = -1 - rng.integers(0, 5, size=16 - n_real[t])
+    inp["logp"][torch.from_numpy(idx < 0)] = 7.0   # padding log-values are ignored
+    inp["idx"] = torch.from_numpy(idx)
+    gpu = run_gpu(inp, chunk=128, temperature=1.5)
+    check_full(inp, gpu, dtype, temperature=1.5)
+
+
+def test_padding_equals_shorter_teacher_rows():
+    # padding at the end of every row == the same rows with K reduced
+    inp = synth.make_custom(300, 64, 700, 12, "bf16", "random5", "uniform", seed=23)
+    short = dict(inp)
+    short["idx"] = inp["idx"][:, :8].contiguous()
+    short["logp"] = inp["logp"][:, :8].contiguous()
+    padded = dict(inp)
+    padded["idx"] = inp["idx"].clone()
+    padded["idx"][:, 8:] = -1
+    a = run_gpu(short, chunk=128, gathered=False)
+    b = run_gpu(padded, chunk=128, gathered=False)
+    assert abs(a["loss"] - b["loss"]) <= 1e-6 * abs(a["loss"])
+    np.testing.assert_allclose(b["row_kl"], a["row_kl"], rtol=1e-5, atol=1e-6)
+    assert np.array_equal(a["lse"], b["lse"])
+    assert rel_fro(b["dH"], a["dH"]) <= 1e-2 and rel_fro(b["dW"], a["dW"]) <= 1e-5
+
+
+def test_bad_temperature_is_an_error():
+    inp = synth.make_custom(64, 64, 300, 4, "bf16", "ones", "uniform", seed=24)
+    with pytest.raises(kd.KdError):
+        run_gpu(inp, temperature=0.0)
+
+
 # ------------------------------------------------------------------ semantics
 def test_all_masked_rows_give_zero():
     inp = synth.make_custom(200, 64, 500, 8, "bf16", "ones", "uniform", seed=9)
