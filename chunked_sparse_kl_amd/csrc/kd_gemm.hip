@@ -821,12 +821,14 @@ __global__ __launch_bounds__(kFusedThreads, 1) void recompute_gemm_kernel(Operan
 constexpr int kPlainWC = KD_PLAIN_WC;          // wavefront columns of the dH / dW tiles
 constexpr int kPlainThreads = 128 * kPlainWC;
 
-template <typename T, bool kAccumulate, bool kAT = false>
+// kGroupM: A tiles per group of the XCD tile walk (dW, whose B = H_c^T is
+// small, prefers 4; dH, 8).
+template <typename T, bool kAccumulate, int kGroupM, bool kAT = false>
 __device__ __attribute__((always_inline)) inline void plain_gemm(char* lds, Operand A, Operand B, int k_elems, int tiles_m,
                                   int tiles_n, int splits, int kb_per_split, float* out,
                                   long long ld_out, long long split_stride, int M, int N) {
   constexpr int BN = TILE_D, WC = kPlainWC, NBJ = BN / (32 * WC);
-  const TileIdx ti = map_tile<8>(tiles_m, tiles_n, splits);
+  const TileIdx ti = map_tile<kGroupM>(tiles_m, tiles_n, splits);
   const int kb_total = (k_elems + Traits<T>::BK - 1) / Traits<T>::BK;
   const int kb0 = ti.split * kb_per_split;
   const int kb1 = min(kb0 + kb_per_split, kb_total);
@@ -897,8 +899,8 @@ __global__ __launch_bounds__(kPlainThreads, 1) void dh_gemm_kernel(Operand A, Op
                                                                     long long ld_out,
                                                                     long long split_stride, int M, int N) {
   KD_DECLARE_LDS(TILE_D);
-  plain_gemm<T, false>(lds, A, B, k_elems, tiles_m, tiles_n, splits, kb_per_split, out, ld_out,
-                       split_stride, M, N);
+  plain_gemm<T, false, 8>(lds, A, B, k_elems, tiles_m, tiles_n, splits, kb_per_split, out, ld_out,
+                          split_stride, M, N);
 }
 
 template <typename T, bool kAccumulate, bool kAT>
@@ -907,8 +909,8 @@ __global__ __launch_bounds__(kPlainThreads, 1) void dw_gemm_kernel(Operand A, Op
                                                                     int kb_per_split, float* out,
                                                                     long long ld_out, int M, int N) {
   KD_DECLARE_LDS(TILE_D);
-  plain_gemm<T, kAccumulate, kAT>(lds, A, B, k_elems, tiles_m, tiles_n, 1, kb_per_split, out, ld_out,
-                                  0, M, N);
+  plain_gemm<T, kAccumulate, 4, kAT>(lds, A, B, k_elems, tiles_m, tiles_n, 1, kb_per_split, out,
+                                     ld_out, 0, M, N);
 }
 
 template <typename T>

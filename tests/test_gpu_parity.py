@@ -38,6 +38,18 @@ def test_small_ragged(dtype, chunk):
     check_full(inp, gpu, dtype)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [320, 288])
+def test_narrow_last_column_tile(dtype, d):
+    # d = 256 + 64 / 256 + 32: the dH and dW tiles of the last 256 hidden
+    # columns take the narrow (64-column) tile path; 4 chunks, so dW is
+    # written by the first pair and accumulated by the second
+    inp = synth.make_custom(700, d, 1100, 24, dtype, "random5", "uniform", seed=25)
+    gpu = run_gpu(inp, chunk=192, grad=1.3)
+    assert gpu["plan"]["n_chunks"] == 4
+    check_full(inp, gpu, dtype, grad=1.3)
+
+
 def test_tiny_fp32_workload_full():
     inp = synth.make_inputs(1)
     gpu = run_gpu(inp, chunk=inp["workload"].chunk)
