@@ -45,15 +45,20 @@ def kernel_traffic(kernel: str):
     return rec["hbm_bytes_per_launch"]
 
 
+def blas_threads() -> int:
+    """Threads of the host BLAS the oracle's matrix products run on."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
 def cpu_baseline(inp: dict, rows: int, seed: int = 3) -> dict:
     """The CPU fp64 oracle, as it stands, on a seeded subset of rows (forward and
     backward of those rows)."""
     from oracle import kl_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+    threads = blas_threads()
     n = inp["H"].shape[0]
     S = np.sort(np.random.default_rng(seed).choice(n, size=rows, replace=False))
     mask = inp["mask"].numpy()
@@ -67,6 +72,87 @@ def cpu_baseline(inp: dict, rows: int, seed: int = 3) -> dict:
                       f"{dt:.1f} s wall"}
 
 
+def roofline_of(stats: list, kernel_traffic_fn) -> dict:
+    """Roofline record of the kernel with the largest summed time."""
+    dom = max(stats, key=lambda s: s["total_ms"])
+    avg_ms = dom["total_ms"] / dom["launches"]
+    if dom["flops"] > 0:
+        achieved = dom["flops"] / dom["launches"] / (avg_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
+    else:
+        achieved = dom["bytes"] / dom["launches"] / (avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof["traffic"] = kernel_traffic_fn(dom["name"])
+    roof["kernel"] = dom["name"]
+    roof["avg_launch_ms"] = round(avg_ms, 4)
+    return roof
+
+
+def topk_builder_main(args) -> int:
+    """Times the teacher top-K cache builder on the 32K-token head shape used as
+    a synthetic teacher (T=32768, d=2880, V=201088, K=100): one build of the
+    whole cache per step, inputs resident in device memory."""
+    import torch
+    import chunked_sparse_kl_amd as kd
+    from chunked_sparse_kl_amd import synth
+
+    dev = torch.device("cuda", 0)
+    w = synth.WORKLOADS[WORKLOAD]
+    log(f"generating inputs: {w.name} (as teacher)")
+    inp = synth.make_inputs(WORKLOAD)
+    Ht, Wt = inp["H"].to(dev), inp["W"].to(dev)
+    T, d, V, K = w.T, w.d, w.V, w.K
+    plan = kd.kd_teacher_topk_plan(kd.KD_BF16, T, d, V, K, args.chunk)
+    log(f"plan: {plan}")
+    ws = torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device=dev)
+    for i in range(args.warmup):
+        idx, logp = kd.kd_teacher_topk(Ht, Wt, K, workspace=ws, plan=plan)
+        log(f"warmup {i + 1}/{args.warmup}")
+    kd.kd_profile_reset()
+    kd.kd_profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        idx, logp = kd.kd_teacher_topk(Ht, Wt, K, workspace=ws, plan=plan)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kd.kd_profile_enable(False)
+    stats = kd.kd_profile_read()
+    ms = elapsed / args.steps * 1e3
+    tflops = 4.0 * T * d * V / (ms * 1e-3) / 1e12
+    for s in sorted(stats, key=lambda s: -s["total_ms"]):
+        log(f"  {s['name']:16s} launches={s['launches']:4d} total={s['total_ms']:9.3f} ms")
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import topk_cache_oracle as TO
+        rows = np.sort(np.random.default_rng(3).choice(T, size=args.cpu_rows_topk, replace=False))
+        t0 = time.perf_counter()
+        ref = TO.build_cache(inp["H"], inp["W"], K, rows=rows)
+        dt = time.perf_counter() - t0
+        assert (ref["logp"] <= 0).all()
+        cpu = {"value": rows.size / dt, "unit": "tokens/s", "cores": blas_threads(),
+               "kind": "oracle", "sample": f"{rows.size} seeded rows of the same shape, fp64, "
+                                           f"{dt:.1f} s wall"}
+        log(f"cpu baseline: {cpu}")
+    out = {
+        "metric": "teacher top-K cache build tokens/s", "value": round(T * args.steps / elapsed, 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"teacher top-K cache T={T} d={d} V={V} K={K}", "T": T, "d": d,
+                   "V": V, "K": K, "chunk": plan["chunk"], "cap": plan["cap"],
+                   "parallelism": "single GPU"},
+        "tflops": round(tflops, 1), "pct_bf16_peak": round(100 * tflops / BF16_PEAK_TFLOPS, 2),
+        "kernels": {s["name"]: {"launches": s["launches"], "total_ms": round(s["total_ms"], 3)}
+                    for s in stats},
+        "roofline": roofline_of(stats, kernel_traffic), "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -77,6 +163,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (3 times), to scale HBM byte counters")
+    ap.add_argument("--topk-builder", action="store_true",
+                    help="time the teacher top-K cache builder instead of the loss step")
+    ap.add_argument("--cpu-rows-topk", type=int, default=512, help="rows of the builder's oracle sample")
     args = ap.parse_args()
     if args.copy_calibration:
         import torch
@@ -89,9 +178,11 @@ def main() -> int:
         print(json.dumps({"copy_bytes": src.numel() * 4, "copies": 3}), flush=True)
         return 0
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: the loss head is measured on a single MI355X "
-              "(see the sharding notes in DESIGN.md); --gpus must be 1", file=sys.stderr)
+        print("bench.py runs on one GPU only: the loss head is measured on a single MI355X; "
+              "--gpus must be 1", file=sys.stderr)
         return 2
+    if args.topk_builder:
+        return topk_builder_main(args)
 
     import torch
     import chunked_sparse_kl_amd as kd
@@ -145,19 +236,7 @@ def main() -> int:
         log(f"  {s['name']:16s} launches={s['launches']:4d} total={s['total_ms']:9.3f} ms "
             f"avg={s['total_ms'] / s['launches']:8.3f} ms "
             f"{(s['flops'] / (s['total_ms'] * 1e-3) / 1e12) if s['flops'] else 0:8.1f} TFLOP/s")
-    dom = kernels[0]
-    avg_ms = dom["total_ms"] / dom["launches"]
-    if dom["flops"] > 0:
-        achieved = dom["flops"] / dom["launches"] / (avg_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
-    else:
-        achieved = dom["bytes"] / dom["launches"] / (avg_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    roof["traffic"] = kernel_traffic(dom["name"])
-    roof["kernel"] = dom["name"]
-    roof["avg_launch_ms"] = round(avg_ms, 4)
+    roof = roofline_of(stats, kernel_traffic)
 
     cpu = None
     if not args.no_cpu_baseline:

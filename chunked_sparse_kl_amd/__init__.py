@@ -20,6 +20,7 @@ __all__ = [
     "KD_BF16", "KD_F32", "KdError", "kd_plan_query", "kd_fused_chunked_kl_fwd",
     "kd_fused_chunked_kl_bwd", "kd_set_validate", "kd_profile_enable", "kd_profile_reset",
     "kd_profile_read", "fused_chunked_kl", "library_path", "EXPORTED_SYMBOLS", "lib",
+    "kd_teacher_topk_plan", "kd_teacher_topk",
 ]
 
 KD_BF16 = 0
@@ -30,6 +31,7 @@ EXPORTED_SYMBOLS = (
     "kd_plan_query", "kd_fused_chunked_kl_fwd", "kd_fused_chunked_kl_bwd", "kd_status_string",
     "kd_last_error_message", "kd_set_validate", "kd_profile_enable", "kd_profile_reset",
     "kd_profile_read",
+    "kd_teacher_topk_plan", "kd_teacher_topk",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -50,6 +52,13 @@ class KdPlan(ctypes.Structure):
         ("chunk", ctypes.c_int64), ("n_chunks", ctypes.c_int64), ("vocab_tiles", ctypes.c_int64),
         ("dh_splits", ctypes.c_int64), ("fwd_workspace_bytes", ctypes.c_size_t),
         ("bwd_workspace_bytes", ctypes.c_size_t), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class KdTopkPlan(ctypes.Structure):
+    _fields_ = [
+        ("chunk", ctypes.c_int64), ("n_chunks", ctypes.c_int64), ("cap", ctypes.c_int64),
+        ("vocab_tiles", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -82,8 +91,12 @@ def _load():
     lib.kd_profile_enable.argtypes = [ctypes.c_int]
     lib.kd_profile_reset.argtypes = []
     lib.kd_profile_read.argtypes = [ctypes.POINTER(KdKernelStat), ctypes.c_int]
+    lib.kd_teacher_topk_plan.argtypes = [ctypes.c_int, i64, i64, i64, i32, i64, i64, sz,
+                                         ctypes.POINTER(KdTopkPlan)]
+    lib.kd_teacher_topk.argtypes = [ctypes.c_int, vp, vp, i64, i64, i64, i32, i64, i64, vp, sz, vp, vp, vp]
     for f in ("kd_plan_query", "kd_fused_chunked_kl_fwd", "kd_fused_chunked_kl_bwd",
-              "kd_set_validate", "kd_profile_enable", "kd_profile_reset", "kd_profile_read"):
+              "kd_set_validate", "kd_profile_enable", "kd_profile_reset", "kd_profile_read",
+              "kd_teacher_topk_plan", "kd_teacher_topk"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -205,6 +218,40 @@ def kd_fused_chunked_kl_bwd(H, W, topk_idx, topk_logp, mask, lse, grad_loss=None
         1 if accumulate else 0,
         _ptr(ws), ws.numel() * ws.element_size(), _stream(H.device)))
     return dH, dW
+
+
+def kd_teacher_topk_plan(dtype: int, n: int, d: int, V: int, K: int, chunk: int = 0, cap: int = 0,
+                         hbm_budget: int = 0) -> dict:
+    """Plan of the teacher top-K cache builder (see kd_teacher_topk_plan in include/kdloss.h)."""
+    out = KdTopkPlan()
+    _check(lib().kd_teacher_topk_plan(dtype, n, d, V, K, chunk, cap, hbm_budget, ctypes.byref(out)))
+    return {f: getattr(out, f) for f, _ in KdTopkPlan._fields_}
+
+
+def kd_teacher_topk(Ht, Wt, K: int, chunk: int = 0, cap: int = 0, workspace=None,
+                    plan: dict | None = None):
+    """Teacher top-K cache of the rows of Ht: (topk_idx [n, K] int32, topk_logp [n, K] fp32),
+    ids in decreasing order of the logit Ht . Wt[v], values the full-vocabulary
+    log-probabilities.  Synchronises the current stream (an offline step)."""
+    if not (Ht.is_cuda and Wt.is_cuda):
+        raise ValueError("Ht and Wt must be device tensors")
+    if Ht.dtype != Wt.dtype:
+        raise TypeError("Ht and Wt must share one dtype")
+    if not (Ht.is_contiguous() and Wt.is_contiguous()):
+        raise ValueError("Ht and Wt must be contiguous")
+    n, d = Ht.shape
+    V = Wt.shape[0]
+    if Wt.shape[1] != d:
+        raise ValueError("shape mismatch between Ht [n, d] and Wt [V, d]")
+    dt = _dtype_code(Ht)
+    plan = plan or kd_teacher_topk_plan(dt, n, d, V, K, chunk, cap)
+    ws = _workspace(plan["workspace_bytes"], Ht.device, workspace)
+    idx = torch.empty((n, K), dtype=torch.int32, device=Ht.device)
+    logp = torch.empty((n, K), dtype=torch.float32, device=Ht.device)
+    _check(lib().kd_teacher_topk(dt, _ptr(Ht), _ptr(Wt), n, d, V, K, plan["chunk"], plan["cap"], _ptr(ws),
+                                 ws.numel() * ws.element_size(), _ptr(idx), _ptr(logp),
+                                 _stream(Ht.device)))
+    return idx, logp
 
 
 def kd_set_validate(on: bool) -> None:

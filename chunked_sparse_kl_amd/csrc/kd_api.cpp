@@ -335,6 +335,92 @@ int prepare_teacher(const Layout& L, const int32_t* idx, const float* logp, cons
   return KD_OK;
 }
 
+// ------------------------------------------------------------------ teacher top-K cache builder
+struct TopkLayout {
+  DType dt;
+  int64_t n, d, V, K, chunk, cap, n_vt, n_rb;
+  size_t ctrl, zero_hits, part, lse, thr, cnt, cand, end;
+};
+
+TopkLayout make_topk_layout(DType dt, int64_t n, int64_t d, int64_t V, int64_t K, int64_t chunk,
+                            int64_t cap) {
+  TopkLayout L{};
+  L.dt = dt;
+  L.n = n;
+  L.d = d;
+  L.V = V;
+  L.K = K;
+  L.chunk = chunk;
+  L.cap = cap;
+  L.n_vt = (V + kd::TILE_V - 1) / kd::TILE_V;
+  L.n_rb = (chunk + kd::ROW_BLOCK - 1) / kd::ROW_BLOCK;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  L.ctrl = take(sizeof(kd::Ctrl));
+  // empty teacher-hit buckets for the statistics pass (zero offsets; the hit
+  // array they index is never read)
+  L.zero_hits = take(size_t(L.n_rb + 1) * (L.n_vt + 1) * 4);
+  L.part = take(size_t(L.n_vt) * chunk * 8);
+  L.lse = take(size_t(chunk) * 4);
+  L.thr = take(size_t(chunk) * 4);
+  L.cnt = take(size_t(chunk) * 4);
+  L.cand = take(size_t(chunk) * cap * 8);
+  L.end = o;
+  return L;
+}
+
+int topk_plan(int dtype, int64_t n, int64_t d, int64_t V, int64_t K, int64_t chunk, int64_t cap,
+              size_t budget_in, TopkLayout* out) {
+  int rc = check_sizes(dtype, n, d, V, K);
+  if (rc != KD_OK) return rc;
+  if (K > kd::kMaxTopkK)
+    return fail(KD_E_INVAL, "K=%lld exceeds the builder's maximum of %d", (long long)K, kd::kMaxTopkK);
+  const int64_t n_vt = (V + kd::TILE_V - 1) / kd::TILE_V;
+  if (n_vt > kd::kMaxTopkTiles)
+    return fail(KD_E_INVAL, "V=%lld exceeds the builder's vocabulary of %lld", (long long)V,
+                (long long)kd::kMaxTopkTiles * kd::TILE_V);
+  // Fewer tiles than K: no tile threshold, every logit is a candidate.
+  if (cap <= 0) cap = n_vt < K ? V : std::min<int64_t>(V, 4096);
+  cap = std::min(cap, V);
+  if (cap < K) return fail(KD_E_INVAL, "cap=%lld must be at least K=%lld", (long long)cap, (long long)K);
+  int64_t c = 0;
+  rc = resolve_chunk(n, chunk, &c);
+  if (rc != KD_OK) return rc;
+  const DType dt = static_cast<DType>(dtype);
+  if (c > 0) {
+    *out = make_topk_layout(dt, n, d, V, K, c, cap);
+    return KD_OK;
+  }
+  size_t budget = budget_in;
+  if (budget == 0) {
+    size_t free_b = 0, total_b = 0;
+    hipError_t e = hipMemGetInfo(&free_b, &total_b);
+    if (e != hipSuccess) return fail(KD_E_HIP, "hipMemGetInfo: %s", hipGetErrorString(e));
+    budget = free_b / 2;
+  }
+  budget = std::min(budget, kWorkspaceCap);
+  if (n <= 256) {
+    *out = make_topk_layout(dt, n, d, V, K, n, cap);
+    if (out->end > budget)
+      return fail(KD_E_WORKSPACE, "workspace of %zu bytes exceeds the budget of %zu bytes", out->end, budget);
+    return KD_OK;
+  }
+  for (int64_t cc = std::min<int64_t>(kMaxAutoChunk, round_up(n, 256)); cc >= 256; cc -= 256) {
+    TopkLayout L = make_topk_layout(dt, n, d, V, K, std::min(cc, n), cap);
+    if (L.end <= budget) {
+      *out = L;
+      return KD_OK;
+    }
+  }
+  TopkLayout L = make_topk_layout(dt, n, d, V, K, 256, cap);
+  return fail(KD_E_WORKSPACE, "no chunk size fits: the smallest plan (chunk 256) needs %zu bytes, budget %zu",
+              L.end, budget);
+}
+
 }  // namespace
 
 extern "C" {
@@ -545,6 +631,89 @@ int kd_fused_chunked_kl_bwd(int dtype, const void* H, const void* W, const int32
       pair_rows = 0;
     }
   }
+  return ok();
+}
+
+int kd_teacher_topk_plan(int dtype, int64_t n, int64_t d, int64_t V, int32_t K, int64_t chunk,
+                         int64_t cap, size_t hbm_budget, kd_topk_plan_t* out) {
+  if (out == nullptr) return fail(KD_E_INVAL, "out must be non-null");
+  TopkLayout L;
+  int rc = topk_plan(dtype, n, d, V, K, chunk, cap, hbm_budget, &L);
+  if (rc != KD_OK) return rc;
+  out->chunk = L.chunk;
+  out->n_chunks = (L.n + L.chunk - 1) / L.chunk;
+  out->cap = L.cap;
+  out->vocab_tiles = L.n_vt;
+  out->workspace_bytes = L.end;
+  return ok();
+}
+
+int kd_teacher_topk(int dtype, const void* Ht, const void* Wt, int64_t n, int64_t d, int64_t V,
+                    int32_t K, int64_t chunk, int64_t cap, void* workspace, size_t workspace_bytes,
+                    int32_t* topk_idx, float* topk_logp, void* stream) {
+  TopkLayout L;
+  int rc = topk_plan(dtype, n, d, V, K, chunk, cap, workspace_bytes ? workspace_bytes : 1, &L);
+  if (rc != KD_OK) return rc;
+  if (Ht == nullptr || Wt == nullptr || topk_idx == nullptr || topk_logp == nullptr)
+    return fail(KD_E_INVAL, "Ht, Wt, topk_idx and topk_logp must be non-null");
+  if (!aligned16(Ht) || !aligned16(Wt)) return fail(KD_E_INVAL, "Ht and Wt must be 16-byte aligned");
+  if (workspace == nullptr || workspace_bytes < L.end)
+    return fail(KD_E_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", L.end, workspace_bytes,
+                workspace == nullptr ? " (null pointer)" : "");
+  if (!aligned16(workspace)) return fail(KD_E_INVAL, "workspace must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  auto* ctrl = reinterpret_cast<kd::Ctrl*>(ws + L.ctrl);
+  auto* zero_hits = reinterpret_cast<int*>(ws + L.zero_hits);
+  auto* part = reinterpret_cast<float2*>(ws + L.part);
+  auto* lse = reinterpret_cast<float*>(ws + L.lse);
+  auto* thr = reinterpret_cast<float*>(ws + L.thr);
+  auto* cnt = reinterpret_cast<int*>(ws + L.cnt);
+  auto* cand = reinterpret_cast<int2*>(ws + L.cand);
+  const size_t es = kd::elem_size(L.dt);
+  KD_LAUNCH("fill", 0, 0, kd::launch_fill_i32(reinterpret_cast<int*>(ctrl), 64, 0, s));
+  KD_LAUNCH("fill", 0, 0,
+            kd::launch_fill_i32(zero_hits, (long long)(L.n_rb + 1) * (L.n_vt + 1), 0, s));
+  for (int64_t c0 = 0; c0 < L.n; c0 += L.chunk) {
+    const int rows = (int)std::min<int64_t>(L.chunk, L.n - c0);
+    const char* Hc = static_cast<const char*>(Ht) + c0 * L.d * es;
+    const double fl = 2.0 * rows * L.d * L.V;
+    const double by = double(L.V) * L.d * es + double(rows) * L.d * es;
+    kd::FwdEpilogue ep{};
+    ep.part = part;
+    ep.ld_part = (int)L.chunk;
+    ep.n_vt = (int)L.n_vt;
+    ep.c0 = 0;  // bucket keys are chunk-local here; every bucket is empty
+    ep.rows = rows;
+    ep.V = (int)L.V;
+    ep.K = (int)L.K;
+    ep.hit_ld = (int)L.n_vt + 1;
+    ep.hit_off = zero_hits;
+    ep.hits = reinterpret_cast<const kd::Hit*>(zero_hits);
+    ep.g = nullptr;
+    ep.inv_tau = 1.0f;
+    KD_LAUNCH("topk_stats_gemm", fl, by + double(rows) * L.n_vt * 8,
+              kd::launch_fwd_gemm(L.dt, Wt, (int)L.V, Hc, rows, (int)L.d, ep, s));
+    KD_LAUNCH("topk_threshold", 0, double(rows) * (L.n_vt * 8 + 8),
+              kd::launch_topk_threshold(part, (int)L.chunk, (int)L.n_vt, (int)L.K, rows, lse, thr, s));
+    KD_LAUNCH("fill", 0, 0, kd::launch_fill_i32(cnt, rows, 0, s));
+    kd::CandEpilogue ce{thr, cnt, cand, (int)L.cap, (int)L.V, rows};
+    KD_LAUNCH("topk_cand_gemm", fl, by, kd::launch_topk_cand_gemm(L.dt, Wt, (int)L.V, Hc, rows, (int)L.d, ce, s));
+    KD_LAUNCH("topk_select", 0, double(rows) * L.K * 8,
+              kd::launch_topk_select(cand, (int)L.cap, cnt, lse, (int)L.K, rows, (int)c0, topk_idx,
+                                     topk_logp, ctrl, s));
+  }
+  // An offline step: wait once, at the end, to report rows whose candidate
+  // list overflowed (their entries are then incomplete).
+  kd::Ctrl host{};
+  hipError_t e = hipMemcpyAsync(&host, ctrl, sizeof(int) * 3, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(KD_E_HIP, "overflow read-back: %s", hipGetErrorString(e));
+  if (host.overflow_rows > 0)
+    return fail(KD_E_RANGE,
+                "%d rows have more than cap=%lld logits at or above their top-K threshold "
+                "(near-constant rows); their entries are incomplete: raise cap",
+                host.overflow_rows, (long long)L.cap);
   return ok();
 }
 

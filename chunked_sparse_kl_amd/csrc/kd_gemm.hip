@@ -813,6 +813,43 @@ __global__ __launch_bounds__(kFusedThreads, 1) void recompute_gemm_kernel(Operan
   }
 }
 
+// ------------------------------------------------------------------ top-K candidates
+// D[v][t] = z_{t,v}, the same main loop as the forward statistics pass, so the
+// logits are bitwise those whose tile maxima set the thresholds.  Each logit
+// at or above its row's threshold is appended to the row's list (an atomic
+// cursor per row; a few hundred entries per row at V = 201088, K = 100).
+template <typename T>
+__global__ __launch_bounds__(kFusedThreads, 1) void topk_cand_gemm_kernel(Operand A, Operand B,
+                                                                           int k_elems, int tiles_m,
+                                                                           int tiles_n, CandEpilogue ep) {
+  constexpr int BN = 256, NBJ = kFusedNBJ, WC = kFusedWC;
+  KD_DECLARE_LDS(BN);
+  const TileIdx ti = map_tile<4>(tiles_m, tiles_n, 1);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave / WC, wc = wave % WC, r32 = lane & 31, h = lane >> 5;
+  f32x16 acc[4][NBJ];
+  const int kb_end = (k_elems + Traits<T>::BK - 1) / Traits<T>::BK;
+  gemm_mainloop<T, BN, WC>(A, B, k_elems, ti.tm, ti.tn, 0, kb_end, lds, acc);
+  const int v_base = ti.tm * BM + wr * 128 + 4 * h;  // + bi*32 + 8*(e/4) + e%4
+#pragma unroll
+  for (int bj = 0; bj < NBJ; ++bj) {
+    const int n = ti.tn * BN + wc * 64 + bj * 32 + r32;
+    const float t = n < ep.rows ? ep.thr[n] : __builtin_inff();
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int v = v_base + bi * 32 + 8 * (e >> 2) + (e & 3);
+        const float z = acc[bi][bj][e];
+        if (z >= t && v < ep.V) {
+          const int slot = atomicAdd(&ep.cnt[n], 1);
+          if (slot < ep.cap) ep.cand[(long long)n * ep.cap + slot] = make_int2(v, __builtin_bit_cast(int, z));
+        }
+      }
+  }
+}
+
 // ------------------------------------------------------------------ dH, dW
 // Plain tiles: D[m][n] (n contiguous in the output).  kAccumulate: out += D.
 #ifndef KD_PLAIN_WC
@@ -938,7 +975,23 @@ void recompute_impl(const void* W, int V, const void* Hc, int rows, int d,
       make_operand<T>(W, d, V), make_operand<T>(Hc, d, rows), d, tiles_m, tiles_n, ep);
 }
 
+template <typename T>
+void topk_cand_impl(const void* Wt, int V, const void* Hc, int rows, int d, const CandEpilogue& ep,
+                    hipStream_t s) {
+  const int tiles_m = (V + BM - 1) / BM, tiles_n = (rows + 255) / 256;
+  topk_cand_gemm_kernel<T><<<tiles_m * tiles_n, kFusedThreads, 0, s>>>(
+      make_operand<T>(Wt, d, V), make_operand<T>(Hc, d, rows), d, tiles_m, tiles_n, ep);
+}
+
 }  // namespace
+
+void launch_topk_cand_gemm(DType t, const void* Wt, int V, const void* Hc, int rows, int d,
+                           const CandEpilogue& ep, hipStream_t s) {
+  if (t == DType::BF16)
+    topk_cand_impl<__bf16>(Wt, V, Hc, rows, d, ep, s);
+  else
+    topk_cand_impl<float>(Wt, V, Hc, rows, d, ep, s);
+}
 
 void launch_fwd_gemm(DType t, const void* W, int V, const void* Hc, int rows, int d,
                      const FwdEpilogue& ep, hipStream_t s) {

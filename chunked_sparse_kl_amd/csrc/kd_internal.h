@@ -23,7 +23,8 @@ constexpr int KBLOCK_BYTES = 128;  // bytes of K per staged GEMM row (64 bf16 / 
 struct Ctrl {
   int n_valid;       // number of unmasked rows
   int range_error;   // 1 if an unmasked row had an id outside [0, V)
-  int pad[62];
+  int overflow_rows; // top-K builder: rows with more candidates than their list holds
+  int pad[61];
 };
 
 enum class DType { BF16 = 0, F32 = 1 };
@@ -119,5 +120,30 @@ void launch_dw_gemm(DType t, const void* GT, int V, int k_len, long long ld_gt, 
 // dW[V][d] (+)= G^T * H.
 void launch_dw_gemm_kmajor(const void* G, int V, int v_pad, int k_len, long long ld_g, const void* HT,
                            int d, long long ld_ht, float* dW, bool accumulate, hipStream_t s);
+
+// ---------------------------------------------------------------- teacher top-K cache builder
+struct CandEpilogue {
+  const float* thr;    // [rows] threshold of each chunk row
+  int* cnt;            // [rows] candidates seen (may exceed cap)
+  int2* cand;          // [rows][cap] (id, logit bits)
+  int cap;
+  int V;
+  int rows;
+};
+// Z = Wt * Ht_c^T over one chunk; every logit >= thr of its row is appended
+// to that row's candidate list (the GEMM is the forward one, bit for bit).
+void launch_topk_cand_gemm(DType t, const void* Wt, int V, const void* Hc, int rows, int d,
+                           const CandEpilogue& ep, hipStream_t s);
+// Per chunk row: LSE from the (max, sum-exp) partials, thr = the K-th largest
+// tile maximum (-inf when there are fewer than K tiles).  n_vt <= kMaxTopkTiles.
+constexpr int kMaxTopkTiles = 15360;  // LDS of the threshold kernel (60 KB of tile keys)
+void launch_topk_threshold(const float2* part, int ld_part, int n_vt, int K, int rows, float* lse,
+                           float* thr, hipStream_t s);
+// Per chunk row: the K candidates with the largest logits (ties by smaller
+// id), in decreasing order, as ids and logit - LSE at rows c0 + r of the
+// outputs; rows whose count exceeds cap are counted in ctrl->overflow_rows.
+constexpr int kMaxTopkK = 4096;  // LDS of the final sort (32 KB of keys)
+void launch_topk_select(const int2* cand, int cap, const int* cnt, const float* lse, int K, int rows,
+                        int c0, int* out_idx, float* out_logp, Ctrl* ctrl, hipStream_t s);
 
 }  // namespace kd

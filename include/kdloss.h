@@ -59,7 +59,8 @@ enum {
   KD_E_INVAL = -1,     /* null pointer, size <= 0, K > V, misalignment, bad dtype or chunk */
   KD_E_WORKSPACE = -2, /* workspace too small (the message gives the bytes needed) or no plan fits */
   KD_E_HIP = -3,       /* a HIP runtime call or kernel launch failed */
-  KD_E_RANGE = -4      /* a teacher id outside [0, V) on an unmasked row (validation mode only) */
+  KD_E_RANGE = -4      /* a teacher id >= V on an unmasked row (validation mode only);
+                          kd_teacher_topk: a row's candidate list overflowed */
 };
 
 /* Result of the chunk and workspace planner. */
@@ -137,6 +138,56 @@ int kd_fused_chunked_kl_bwd(int dtype, const void* H, const void* W, const int32
                             int64_t V, int32_t K, int64_t chunk, float temperature, const float* lse,
                             const float* grad_loss, void* dH, float* dW, int accumulate_dw,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Teacher top-K cache builder: the offline cache the loss above consumes.
+ * The pages keep, for every position, the K most likely tokens of the
+ * teacher, computed once (Hugging Face blog "Making Knowledge Distillation
+ * Cheap Enough to Run at Scale", section "Two systems changes"; aimodeling.com
+ * article, section "First cut: remove the teacher from the training loop").
+ * For every row t of the teacher's final hidden states:
+ *   z_{t,v} = Ht[t] . Wt[v]  (fp32 accumulation of dtype products)
+ *   topk_idx[t, :]  the K ids with the largest z_{t,v}, in decreasing order of
+ *                   z; equal logits are taken in increasing id order
+ *   topk_logp[t, :] z_{t,v} - LSE_v(z_t) at those ids (full-vocabulary
+ *                   log-probabilities: the format of topk_idx / topk_logp of
+ *                   the loss calls)
+ * No row's logits are ever stored: each chunk of rows runs the output GEMM
+ * twice, once for LSE and per-tile maxima (the K-th largest tile maximum is a
+ * threshold that every top-K logit reaches), once to collect the logits at or
+ * above the threshold into a per-row list of at most `cap` entries.
+ *
+ * Plan: chunk as for kd_plan_query (<= 0: the planner picks the largest that
+ * fits hbm_budget, 0 = half the free device memory); cap <= 0 picks
+ * min(V, 4096), or V when V has fewer than K 256-wide tiles; cap >= K.
+ */
+typedef struct kd_topk_plan {
+  int64_t chunk;
+  int64_t n_chunks;
+  int64_t cap;              /* candidate-list entries per row */
+  int64_t vocab_tiles;
+  size_t workspace_bytes;   /* needed by kd_teacher_topk */
+} kd_topk_plan_t;
+
+int kd_teacher_topk_plan(int dtype, int64_t n, int64_t d, int64_t V, int32_t K, int64_t chunk,
+                         int64_t cap, size_t hbm_budget, kd_topk_plan_t* out);
+
+/*
+ *   Ht        [n, d]  dtype device   teacher hidden states (16-byte aligned)
+ *   Wt        [V, d]  dtype device   teacher output-projection weight
+ *   K         1 <= K <= min(V, 4096)
+ *   topk_idx  [n, K]  int32 device, written
+ *   topk_logp [n, K]  fp32 device, written
+ *   workspace device buffer of at least plan.workspace_bytes (uninitialised)
+ * Unlike the loss calls this one synchronises `stream` before returning: it
+ * returns KD_E_RANGE if some row had more than cap logits at or above its
+ * threshold (only for rows of nearly constant logits); those rows' entries are
+ * then incomplete and the call should be repeated with a larger cap.  NaN
+ * logits are unsupported (such a row may come back with ids of -1).
+ */
+int kd_teacher_topk(int dtype, const void* Ht, const void* Wt, int64_t n, int64_t d, int64_t V,
+                    int32_t K, int64_t chunk, int64_t cap, void* workspace, size_t workspace_bytes,
+                    int32_t* topk_idx, float* topk_logp, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* kd_status_string(int status);

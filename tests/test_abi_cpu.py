@@ -126,3 +126,34 @@ def test_bad_temperature_rejected_without_device_work(tau):
     rc = lib.kd_fused_chunked_kl_bwd(0, fake, fake, fake, fake, None, 256, 256, 4096, 16, 64, tau, fake,
                                      fake, fake, fake, 1, fake, 1 << 30, None)
     assert rc == -1 and b"temperature" in lib.kd_last_error_message()
+
+
+# ------------------------------------------------------------------ teacher top-K cache builder
+def test_topk_plan_defaults():
+    p = kd.kd_teacher_topk_plan(kd.KD_BF16, 32768, 2880, 201088, 100, 0, 0, GiB * 8)
+    assert p["cap"] == 4096 and p["vocab_tiles"] == 786 and p["chunk"] % 256 == 0
+    assert p["workspace_bytes"] <= GiB * 8
+    # fewer 256-wide tiles than K: every logit is a candidate
+    p = kd.kd_teacher_topk_plan(kd.KD_F32, 700, 192, 1100, 24, 256, 0, GiB)
+    assert p["cap"] == 1100 and p["chunk"] == 256 and p["n_chunks"] == 3
+    p = kd.kd_teacher_topk_plan(kd.KD_F32, 700, 192, 8000, 24, 0, 100, GiB)
+    assert p["cap"] == 100
+
+
+@pytest.mark.parametrize("kwargs", [dict(K=5000), dict(cap=10), dict(chunk=100), dict(V=10), dict(d=250)])
+def test_topk_plan_rejects(kwargs):
+    args = dict(dtype=kd.KD_BF16, n=1000, d=256, V=8000, K=24, chunk=0, cap=0)
+    args.update(kwargs)
+    with pytest.raises(kd.KdError) as e:
+        kd.kd_teacher_topk_plan(args["dtype"], args["n"], args["d"], args["V"], args["K"], args["chunk"],
+                                args["cap"], GiB)
+    assert e.value.status == -1
+
+
+def test_topk_null_pointers_and_small_workspace_rejected_without_device_work():
+    lib = kd.lib()
+    fake = ctypes.c_void_p(4096)
+    rc = lib.kd_teacher_topk(0, None, fake, 256, 256, 4096, 16, 64, 0, fake, 1 << 30, fake, fake, None)
+    assert rc == -1 and b"non-null" in lib.kd_last_error_message()
+    rc = lib.kd_teacher_topk(0, fake, fake, 256, 256, 4096, 16, 64, 0, fake, 16, fake, fake, None)
+    assert rc == -2 and b"workspace" in lib.kd_last_error_message()

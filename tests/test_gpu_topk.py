@@ -1,0 +1,124 @@
+"""GPU parity of the teacher top-K cache builder (through the C ABI) against the
+CPU fp64 oracle.
+
+The GPU's logits carry fp32 accumulation error, so ids are compared where the
+oracle separates them by more than that error: the selected set must be a
+valid top-K of the exact logits (selection margin >= -2 eps), in
+non-increasing order of the exact logit, and equal to the oracle's wherever
+the K-th and (K+1)-th exact logits differ by more than 2 eps.  Exactly tied
+logits (identical weight rows) are tied on both sides and are compared id for
+id (ties by increasing id).
+"""
+import numpy as np
+import pytest
+import torch
+
+import chunked_sparse_kl_amd as kd
+from chunked_sparse_kl_amd import synth
+from oracle import topk_cache_oracle as T
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _name(request):
+    print(f"[case] {request.node.name}", flush=True)
+    yield
+
+
+def _inputs(n, d, V, dtype, seed):
+    g = torch.Generator().manual_seed(seed)
+    Ht = torch.randn(n, d, generator=g)
+    Wt = torch.randn(V, d, generator=g) / d ** 0.5
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    return Ht.to(dt), Wt.to(dt)
+
+
+def _run(Ht, Wt, K, **kw):
+    dev = torch.device("cuda", 0)
+    idx, logp = kd.kd_teacher_topk(Ht.to(dev), Wt.to(dev), K, **kw)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy().astype(np.int64), logp.cpu().double().numpy()
+
+
+def _check(Ht, Wt, K, idx, logp, rows=None, eps=1e-4):
+    ref = T.build_cache(Ht, Wt, K, rows=rows)
+    z, V = ref["z"], ref["z"].shape[1]
+    gi = idx if rows is None else idx[np.asarray(rows)]
+    gl = logp if rows is None else logp[np.asarray(rows)]
+    assert ((gi >= 0) & (gi < V)).all()
+    for t in range(gi.shape[0]):
+        assert np.unique(gi[t]).size == K, t
+    assert (T.selection_margin(z, gi) >= -2 * eps).all()
+    zs = np.take_along_axis(z, gi, axis=1)
+    assert (np.diff(zs, axis=1) <= 2 * eps).all()
+    zsort = -np.sort(-z, axis=1)
+    gap = zsort[:, K - 1] - (zsort[:, K] if K < V else -np.inf)
+    sep = gap > 2 * eps
+    for t in np.nonzero(sep)[0]:
+        assert set(gi[t]) == set(ref["ids"][t]), t
+    np.testing.assert_allclose(gl, zs - ref["lse"][:, None], rtol=0, atol=5 * eps)
+    return ref
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("V,K", [(8000, 24), (1100, 24), (8000, 1)])
+def test_small_ragged(dtype, V, K):
+    # 8000 / 24: 32 tiles >= K (tile threshold); 1100 / 24: 5 tiles < K (every logit a candidate)
+    Ht, Wt = _inputs(700, 192, V, dtype, seed=31)
+    idx, logp = _run(Ht, Wt, K, chunk=256)
+    _check(Ht, Wt, K, idx, logp)
+
+
+def test_k_equals_v():
+    Ht, Wt = _inputs(130, 64, 300, "bf16", seed=32)
+    idx, logp = _run(Ht, Wt, 300, chunk=64)
+    _check(Ht, Wt, 300, idx, logp)
+
+
+def test_exact_ties_by_increasing_id():
+    # 40 distinct weight rows repeated: logits tie exactly on both sides
+    Ht, base = _inputs(300, 128, 40, "bf16", seed=33)
+    Wt = base[torch.arange(4000) % 40].contiguous()
+    K = 57
+    idx, logp = _run(Ht, Wt, K, chunk=128)
+    ref = T.build_cache(Ht, Wt, K)
+    assert np.array_equal(idx, ref["ids"])
+    np.testing.assert_allclose(logp, ref["logp"], rtol=0, atol=5e-4)
+
+
+def test_clustered_top_values_in_one_tile():
+    # the largest logits of every row sit in one 256-wide tile
+    Ht, Wt = _inputs(256, 64, 5000, "f32", seed=34)
+    Wt[512:768] += 3.0 * Ht.mean(0) / Ht.mean(0).norm()
+    idx, logp = _run(Ht, Wt, 100, chunk=128)
+    _check(Ht, Wt, 100, idx, logp)
+
+
+def test_overflowing_candidate_list_is_an_error():
+    # constant logits: every logit reaches the threshold; with cap = K the list overflows
+    Ht, base = _inputs(64, 64, 1, "bf16", seed=35)
+    Wt = base.repeat(8000, 1).contiguous()
+    with pytest.raises(kd.KdError) as e:
+        _run(Ht, Wt, 24, cap=24)
+    assert e.value.status == -4 and "raise cap" in str(e.value)
+    idx, logp = _run(Ht, Wt, 24, cap=8000)  # a cap that holds the whole row: ties by id
+    assert (idx == np.arange(24)).all()
+
+
+def test_deterministic_repeat():
+    Ht, Wt = _inputs(500, 128, 9000, "bf16", seed=36)
+    a = _run(Ht, Wt, 50, chunk=192)
+    b = _run(Ht, Wt, 50, chunk=192)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_full_size_sampled_rows():
+    # the 32K-token head shape as a synthetic teacher (T=32768, d=2880, V=201088, K=100)
+    inp = synth.make_inputs(4)
+    Ht, Wt = inp["H"], inp["W"]
+    idx, logp = _run(Ht, Wt, 100)
+    rows = np.sort(np.random.default_rng(7).choice(Ht.shape[0], size=8, replace=False))
+    rows = np.concatenate([[0, 8191, 8192, Ht.shape[0] - 1], rows])
+    _check(Ht, Wt, 100, idx, logp, rows=rows, eps=2e-4)
+    assert (np.diff(logp, axis=1) <= 1e-3).all()
