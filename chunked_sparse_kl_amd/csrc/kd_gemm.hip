@@ -124,6 +124,44 @@ __device__ inline TileIdx map_tile(int tiles_m, int tiles_n, int splits) {
   return t;
 }
 
+// Two walks that share tiles across XCDs instead (through the last-level
+// cache), measured faster for the plain GEMMs:
+//  * linear: tile lin = blockIdx, so consecutive tiles run on different XCDs
+//    (dW: every XCD reads the same rows of G at about the same time);
+//  * M-sliced (tiles_m % 8 == 0, else the XCD ranges above): XCD x owns the
+//    M tiles [x * tiles_m / 8, ...) and all XCDs walk the N tiles (then the
+//    splits) in step (dH: every XCD reads the same W^T tiles).
+template <int kGroupM>
+__device__ inline TileIdx map_tile_linear(int tiles_m, int tiles_n, int splits) {
+  const int lin = blockIdx.x;
+  const int per_split = tiles_m * tiles_n;
+  TileIdx t;
+  t.split = lin / per_split;
+  const int r = lin - t.split * per_split;
+  const int span = kGroupM * tiles_n;
+  const int group = r / span;
+  const int first_m = group * kGroupM;
+  const int gsize = min(tiles_m - first_m, kGroupM);
+  const int w = r - group * span;
+  t.tm = first_m + w % gsize;
+  t.tn = w / gsize;
+  return t;
+}
+
+template <int kGroupM>
+__device__ inline TileIdx map_tile_msliced(int tiles_m, int tiles_n, int splits) {
+  if ((tiles_m & 7) != 0) return map_tile<kGroupM>(tiles_m, tiles_n, splits);
+  const int xcd = blockIdx.x & 7, l = blockIdx.x >> 3;
+  const int mpx = tiles_m >> 3;
+  const int per = mpx * tiles_n;
+  TileIdx t;
+  t.split = l / per;
+  const int r = l - t.split * per;
+  t.tm = xcd * mpx + r % mpx;
+  t.tn = r / mpx;
+  return t;
+}
+
 template <typename T>
 __device__ inline void mma_block(const uint4& a, const uint4& b, f32x16& acc);
 
@@ -858,14 +896,16 @@ __global__ __launch_bounds__(kFusedThreads, 1) void topk_cand_gemm_kernel(Operan
 constexpr int kPlainWC = KD_PLAIN_WC;          // wavefront columns of the dH / dW tiles
 constexpr int kPlainThreads = 128 * kPlainWC;
 
-// kGroupM: A tiles per group of the XCD tile walk (dW, whose B = H_c^T is
-// small, prefers 4; dH, 8).
-template <typename T, bool kAccumulate, int kGroupM, bool kAT = false>
+// Tile walks of the plain GEMMs (measured per kernel).
+enum class Walk { kMSliced, kLinear };
+
+template <typename T, bool kAccumulate, Walk kWalk, bool kAT = false>
 __device__ __attribute__((always_inline)) inline void plain_gemm(char* lds, Operand A, Operand B, int k_elems, int tiles_m,
                                   int tiles_n, int splits, int kb_per_split, float* out,
                                   long long ld_out, long long split_stride, int M, int N) {
   constexpr int BN = TILE_D, WC = kPlainWC, NBJ = BN / (32 * WC);
-  const TileIdx ti = map_tile<kGroupM>(tiles_m, tiles_n, splits);
+  const TileIdx ti = kWalk == Walk::kMSliced ? map_tile_msliced<8>(tiles_m, tiles_n, splits)
+                                             : map_tile_linear<4>(tiles_m, tiles_n, splits);
   const int kb_total = (k_elems + Traits<T>::BK - 1) / Traits<T>::BK;
   const int kb0 = ti.split * kb_per_split;
   const int kb1 = min(kb0 + kb_per_split, kb_total);
@@ -936,8 +976,8 @@ __global__ __launch_bounds__(kPlainThreads, 1) void dh_gemm_kernel(Operand A, Op
                                                                     long long ld_out,
                                                                     long long split_stride, int M, int N) {
   KD_DECLARE_LDS(TILE_D);
-  plain_gemm<T, false, 8>(lds, A, B, k_elems, tiles_m, tiles_n, splits, kb_per_split, out, ld_out,
-                          split_stride, M, N);
+  plain_gemm<T, false, Walk::kMSliced>(lds, A, B, k_elems, tiles_m, tiles_n, splits, kb_per_split,
+                                       out, ld_out, split_stride, M, N);
 }
 
 template <typename T, bool kAccumulate, bool kAT>
@@ -946,8 +986,8 @@ __global__ __launch_bounds__(kPlainThreads, 1) void dw_gemm_kernel(Operand A, Op
                                                                     int kb_per_split, float* out,
                                                                     long long ld_out, int M, int N) {
   KD_DECLARE_LDS(TILE_D);
-  plain_gemm<T, kAccumulate, 4, kAT>(lds, A, B, k_elems, tiles_m, tiles_n, 1, kb_per_split, out,
-                                     ld_out, 0, M, N);
+  plain_gemm<T, kAccumulate, Walk::kLinear, kAT>(lds, A, B, k_elems, tiles_m, tiles_n, 1, kb_per_split,
+                                                  out, ld_out, 0, M, N);
 }
 
 template <typename T>
