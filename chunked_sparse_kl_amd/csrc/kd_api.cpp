@@ -137,9 +137,10 @@ struct Layout {
 };
 
 // Split-K factor of dH = G W (K = V is long, the output C x d is small): the
-// smallest factor >= 4 whose grid is a whole number of waves over the 256 CUs
-// of an MI355X, else the factor in [4, 16] with the least idle tail; never
-// fewer than 16 K blocks per split.
+// smallest factor >= 2 whose grid is a whole number of waves over the 256 CUs
+// of an MI355X, else the factor in [2, 16] with the least idle tail; never
+// fewer than 16 K blocks per split.  (Fewer splits also mean fewer fp32
+// partials for the reduction.)
 constexpr int kComputeUnits = 256;
 
 int dh_splits(DType dt, int64_t c_pad, int64_t d, int64_t v_pad) {
@@ -149,7 +150,7 @@ int dh_splits(DType dt, int64_t c_pad, int64_t d, int64_t v_pad) {
   const int64_t s_max = std::max<int64_t>(1, std::min<int64_t>(16, kb_total / 16));
   int64_t best = 1;
   double best_eff = -1.0;
-  for (int64_t s = std::min<int64_t>(4, s_max); s <= s_max; ++s) {
+  for (int64_t s = std::min<int64_t>(2, s_max); s <= s_max; ++s) {
     const double waves = double(tiles * s) / kComputeUnits;
     const double eff = waves / std::ceil(waves);
     if (eff > best_eff + 1e-9) {
