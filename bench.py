@@ -153,6 +153,53 @@ def topk_builder_main(args) -> int:
     return 0
 
 
+def memory_sweep_main(args) -> int:
+    """Peak device memory of one fwd+bwd against T at d=3072, V=128256, K=100
+    (the long-context workload's shapes; values are random device tensors:
+    memory does not depend on them), with the planner choosing the chunk.
+    Fits peak = a + b*T by least squares over the sizes at the planner's
+    largest chunk and prints the points, a, b and the largest residual."""
+    import torch
+    import chunked_sparse_kl_amd as kd
+
+    dev = torch.device("cuda", 0)
+    d, V, K = 3072, 128256, 100
+    Ts = [4096, 8192, 16384, 32768, 65536, 131072, 262144]
+    g = torch.Generator(device=dev).manual_seed(5)
+    W = (torch.randn(V, d, device=dev, generator=g) * d ** -0.5).to(torch.bfloat16)
+    pts = []
+    for T in Ts:
+        H = torch.randn(T, d, device=dev, generator=g).to(torch.bfloat16)
+        idx = torch.randint(0, V, (T, K), device=dev, dtype=torch.int32, generator=g)
+        logp = torch.randn(T, K, device=dev, generator=g)
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats(dev)
+        fw = kd.kd_fused_chunked_kl_fwd(H, W, idx, logp, None, row_kl=False)
+        dH, dW = kd.kd_fused_chunked_kl_bwd(H, W, idx, logp, None, fw["lse"], plan=fw["plan"])
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated(dev)
+        pts.append({"T": T, "peak_gib": round(peak / 2**30, 4), "chunk": fw["plan"]["chunk"],
+                    "loss_finite": bool(torch.isfinite(fw["loss"]).item())})
+        log(f"T={T}: peak {peak / 2**30:.3f} GiB, chunk {fw['plan']['chunk']}")
+        del H, idx, logp, fw, dH, dW
+        torch.cuda.empty_cache()
+    # The planner's chunk grows with T up to its maximum; from there on the
+    # workspace is fixed and peak memory is a + b*T.
+    cmax = max(p["chunk"] for p in pts)
+    fit_pts = [p for p in pts if p["chunk"] == cmax]
+    t = np.array([p["T"] for p in fit_pts], dtype=np.float64)
+    y = np.array([p["peak_gib"] for p in fit_pts]) * 2**30
+    b, a = np.polyfit(t, y, 1)
+    resid = y - (a + b * t)
+    out = {"metric": "peak device memory vs tokens (fwd+bwd)", "d": d, "V": V, "K": K, "points": pts,
+           "fit": {"over_T": [p["T"] for p in fit_pts], "chunk": cmax, "a_gib": round(a / 2**30, 4),
+                   "b_bytes_per_token": round(b, 1),
+                   "max_abs_residual_gib": round(float(np.abs(resid).max()) / 2**30, 5)},
+           "full_logits_fp32_gib_at_256k": round(262144 * V * 4 / 2**30, 1)}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -166,6 +213,8 @@ def main() -> int:
     ap.add_argument("--topk-builder", action="store_true",
                     help="time the teacher top-K cache builder instead of the loss step")
     ap.add_argument("--cpu-rows-topk", type=int, default=512, help="rows of the builder's oracle sample")
+    ap.add_argument("--memory-sweep", action="store_true",
+                    help="peak device memory of fwd+bwd against T (4K .. 256K tokens) and its linear fit")
     args = ap.parse_args()
     if args.copy_calibration:
         import torch
@@ -183,6 +232,8 @@ def main() -> int:
         return 2
     if args.topk_builder:
         return topk_builder_main(args)
+    if args.memory_sweep:
+        return memory_sweep_main(args)
 
     import torch
     import chunked_sparse_kl_amd as kd

@@ -890,10 +890,7 @@ __global__ __launch_bounds__(kFusedThreads, 1) void topk_cand_gemm_kernel(Operan
 
 // ------------------------------------------------------------------ dH, dW
 // Plain tiles: D[m][n] (n contiguous in the output).  kAccumulate: out += D.
-#ifndef KD_PLAIN_WC
-#define KD_PLAIN_WC 4
-#endif
-constexpr int kPlainWC = KD_PLAIN_WC;          // wavefront columns of the dH / dW tiles
+constexpr int kPlainWC = 4;                    // wavefront columns of the dH / dW tiles
 constexpr int kPlainThreads = 128 * kPlainWC;
 
 // Tile walks of the plain GEMMs (measured per kernel).
