@@ -205,7 +205,8 @@ Layout make_layout(DType dt, int64_t n, int64_t d, int64_t V, int64_t K, int64_t
   L.g_rows = L.dt == DType::BF16 ? L.gt_cols : L.c_pad;
   L.G = take(size_t(L.g_rows) * L.v_pad * es);
   L.GT = L.dt == DType::BF16 ? o : take(size_t(L.v_pad) * L.gt_cols * es);
-  L.WT = take(size_t(d) * L.v_pad * es);
+  // bf16: dH reads W itself k-major (no W^T); fp32: dH reads W^T.
+  L.WT = L.dt == DType::BF16 ? o : take(size_t(d) * L.v_pad * es);
   L.HT = take(size_t(d) * L.gt_cols * es);
   L.dhpart = take(size_t(L.splits) * L.c_pad * d * 4);
   L.bwd_end = o;
@@ -565,9 +566,11 @@ int kd_fused_chunked_kl_bwd(int dtype, const void* H, const void* W, const int32
   if (rc != KD_OK) return rc;
 
   const size_t es = kd::elem_size(L.dt);
-  KD_LAUNCH("transpose_w", 0, 2.0 * L.V * L.d * es,
-            kd::launch_transpose_pad(L.dt, W, (int)L.V, (int)L.d, L.d, ws + L.WT, (int)L.v_pad,
-                                     L.v_pad, s));
+  const bool w_kmajor = L.dt == DType::BF16;  // dH reads W itself
+  if (!w_kmajor)
+    KD_LAUNCH("transpose_w", 0, 2.0 * L.V * L.d * es,
+              kd::launch_transpose_pad(L.dt, W, (int)L.V, (int)L.d, L.d, ws + L.WT, (int)L.v_pad,
+                                       L.v_pad, s));
   bool dw_written = accumulate_dw != 0;  // later dW launches accumulate
   int pair_rows = 0;                      // unpadded rows of the pair's chunks
   for (int64_t c = 0; c < L.n_chunks; ++c) {
@@ -611,7 +614,7 @@ int kd_fused_chunked_kl_bwd(int dtype, const void* H, const void* W, const int32
     KD_LAUNCH("dh_gemm", fl,
               double(c_pad) * L.v_pad * es + double(L.d) * L.v_pad * es + double(L.splits) * rows * L.d * 4,
               kd::launch_dh_gemm(L.dt, ws + L.G + size_t(g_row0) * L.v_pad * es, rows, (int)L.v_pad,
-                                 ws + L.WT, (int)L.d,
+                                 w_kmajor ? W : ws + L.WT, w_kmajor, (int)L.V, (int)L.d,
                                  (int)L.splits, reinterpret_cast<float*>(ws + L.dhpart),
                                  split_stride, s));
     KD_LAUNCH("dh_reduce", 0, double(L.splits) * rows * L.d * 4 + double(rows) * L.d * es,

@@ -186,6 +186,7 @@ struct Operand {
   const char* base;   // row 0, k 0
   long long ld;       // row pitch in bytes
   int rows;           // rows >= this read as zero
+  int krows;          // k-major B only: k rows present in memory (later ones read as zero)
 };
 
 // Main loop: accumulates the tile (tm, tn) over K blocks [kb0, kb1).
@@ -209,9 +210,12 @@ struct Operand {
 // two such rows, 16-byte chunk c of row k sits at c ^ 4 (k % 4), and the MFMA
 // fragments come from transposing LDS reads (ds_read_b64_tr_b16).  The block's
 // buffer resource is rebased per K block, so the operand may exceed 4 GB.
-template <typename T, int BN, int WC, bool kAT = false>
+// kBT: the same for B ([k][n], n contiguous; bf16 only), whose K extent may
+// end inside the last K block (its range then stops at the last k row).
+template <typename T, int BN, int WC, bool kAT = false, bool kBT = false>
 struct MainLoop {
   static_assert(!kAT || sizeof(T) == 2, "k-major A needs 16-bit elements");
+  static_assert(!kBT || (sizeof(T) == 2 && !kAT), "k-major B: 16-bit elements, A k-contiguous");
   static constexpr int BK = Traits<T>::BK;
   static constexpr int EPC = 16 / sizeof(T);      // elements per 16-byte chunk
   static constexpr int WAVES = 2 * WC;            // 2 wavefront rows x WC columns
@@ -235,6 +239,8 @@ struct MainLoop {
   int k_elems;
   int wave_row;              // wave * 8 (uniform)
   long long a_ld;            // kAT: bytes per k row of A
+  long long b_ldk;           // kBT: bytes per k row of B
+  int b_krows;               // kBT: k rows of B in memory
 
   __device__ inline void init(const Operand& A, const Operand& B, int ke, int tm, int tn) {
     const int lane = threadIdx.x & 63;
@@ -264,14 +270,27 @@ struct MainLoop {
     a_valid = min(A.rows - tm * BM, BM);
     b_valid = min(B.rows - tn * BN, BN);
     a_tile = A.base + (long long)tm * BM * A.ld;
-    b_tile = B.base + (long long)tn * BN * B.ld;
     a_bytes = (unsigned)(a_valid * A.ld);
-    b_bytes = (unsigned)(b_valid * B.ld);
     ra = make_rsrc(a_tile, a_bytes);
-    rb = make_rsrc(b_tile, b_bytes);
     a_off = (unsigned)((wave_row + r) * A.ld + c * 16);
-    b_off = (unsigned)((wave_row + r) * B.ld + c * 16);
     a_step = (unsigned)(ROWS_PER_LD * A.ld);
+    if constexpr (kBT) {
+      // as k-major A: lane L of load i stages k row 16 i + 2 w + L / 32 of
+      // the block, logical chunk (L % 32) ^ 4 (row % 4) of its BN columns
+      static_assert(BN == BM && B_LD == A_LD, "k-major B staging mirrors k-major A");
+      const int row = 2 * w + (lane >> 5);
+      const int cb = (lane & 31) ^ (4 * (row & 3));
+      b_tile = B.base + (long long)tn * BN * (long long)sizeof(T);
+      b_ldk = B.ld;
+      b_krows = B.krows;
+      b_off = (cb * EPC < b_valid) ? (unsigned)(row * B.ld + cb * 16) : kOut;
+      b_step = (unsigned)(16 * B.ld);
+      return;
+    }
+    b_tile = B.base + (long long)tn * BN * B.ld;
+    b_bytes = (unsigned)(b_valid * B.ld);
+    rb = make_rsrc(b_tile, b_bytes);
+    b_off = (unsigned)((wave_row + r) * B.ld + c * 16);
     b_step = (unsigned)(ROWS_PER_LD * B.ld);
   }
 
@@ -290,6 +309,14 @@ struct MainLoop {
     dma16(ra, off, __builtin_amdgcn_readfirstlane(lds_addr(st + (i * ROWS_PER_LD + wave_row) * ROWB)));
   }
   __device__ inline void issue_b(int kb, char* st, bool valid, int i) const {
+    if constexpr (kBT) {
+      const int k0 = kb * BK;
+      const int rows_here = max(0, min(BK, b_krows - k0));  // k rows of this block in memory
+      const i32x4 rk = make_rsrc(b_tile + (long long)k0 * b_ldk, (unsigned)(rows_here * b_ldk));
+      const unsigned off = (valid && b_off != kOut) ? b_off + i * b_step : kOut;
+      dma16(rk, off, __builtin_amdgcn_readfirstlane(lds_addr(st + (16 * i + wave_row / 4) * BN * (int)sizeof(T))));
+      return;
+    }
     const unsigned off = (valid && wave_row + r + ROWS_PER_LD * i < b_valid) ? b_off + i * b_step + (unsigned)kb * ROWB : kOut;
     dma16(rb, off, __builtin_amdgcn_readfirstlane(lds_addr(st + (i * ROWS_PER_LD + wave_row) * ROWB)));
   }
@@ -330,36 +357,48 @@ struct MainLoop {
     uint4 a[4], b[NBJ];
   };
 
+  // Fragments of NBLK 32-wide blocks, starting at column idx0, of a k-major
+  // slot (rows of row_bytes per k).  Lane l of 16-lane group g names k row
+  // kb + (l%16)/4 and columns idx0 + 16 (g%2) + 4 (l % 4) .. +3; the
+  // transposing read hands lane i of the group the 4 k values of column
+  // ... + i.  Two reads give k = 16 s + 8 h .. +7.  k % 4 = (l % 16) / 4 for
+  // every read, so the swizzle term depends on the lane and the block only
+  // and the rest is an immediate offset.
+  template <int NBLK, int kRowBytes>
+  __device__ inline static void tr_frags(const char* slot, int idx0, int s, uint4 (&out)[NBLK]) {
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, q = lane & 15, x = q >> 2;
+    const int m = idx0 + 16 * (g & 1) + 4 * (q & 3);
+    const unsigned base = lds_addr(slot) + (unsigned)((8 * (g >> 1) + x) * kRowBytes + (m & 7) * 2);
+    typedef short v4s __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int bi = 0; bi < NBLK; ++bi) {
+      const unsigned a = base + ((((m >> 3) + 4 * bi) ^ (4 * x)) << 4);
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s*)(a + (16 * s) * kRowBytes));
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s*)(a + (16 * s + 4) * kRowBytes));
+      const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+      out[bi] = uint4{l2.x, l2.y, h2.x, h2.y};
+    }
+  }
+
   // Fragment loads of substep s (16 bf16 / 8 fp32 K elements) from the slots
   // sa (A) and sb (B).
   __device__ inline static void load(const char* sa, const char* sb, int s, Frags& f) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wr = wave / WC, wc = wave % WC;
     const int r32 = lane & 31, h = lane >> 5;
-    const char* b_row0 = sb + (wc * (BN / WC) + r32) * ROWB;
     const int ch = ((2 * s + h) ^ ((r32 >> 1) & 7)) << 4;
+    if constexpr (kBT) {
+      tr_frags<NBJ, BN * 2>(sb, wc * (BN / WC), s, f.b);
+    } else {
+      const char* b_row0 = sb + (wc * (BN / WC) + r32) * ROWB;
 #pragma unroll
-    for (int bj = 0; bj < NBJ; ++bj) f.b[bj] = *reinterpret_cast<const uint4*>(b_row0 + bj * 32 * ROWB + ch);
+      for (int bj = 0; bj < NBJ; ++bj) f.b[bj] = *reinterpret_cast<const uint4*>(b_row0 + bj * 32 * ROWB + ch);
+    }
     if constexpr (kAT) {
-      // Lane l of 16-lane group g names k row kb + (l%16)/4 and columns
-      // m0 + 4 (l % 4) .. +3; the transposing read hands lane i of the group
-      // the 4 k values of column m0 + i.  Two reads give k = 16 s + 8 h .. +7.
-      // k % 4 = (l % 16) / 4 for every read, so the swizzle term depends on
-      // the lane and bi only and the rest is an immediate offset.
-      const int g = lane >> 4, q = lane & 15, x = q >> 2;
-      const int m = wr * 128 + 16 * (g & 1) + 4 * (q & 3);
-      const unsigned base = lds_addr(sa) + (unsigned)((8 * (g >> 1) + x) * (BM * 2) + (m & 7) * 2);
-      typedef short v4s __attribute__((ext_vector_type(4)));
-#pragma unroll
-      for (int bi = 0; bi < 4; ++bi) {
-        const unsigned a = base + ((((m >> 3) + 4 * bi) ^ (4 * x)) << 4);
-        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4s*)(a + (16 * s) * (BM * 2)));
-        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4s*)(a + (16 * s + 4) * (BM * 2)));
-        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-        f.a[bi] = uint4{l2.x, l2.y, h2.x, h2.y};
-      }
+      tr_frags<4, BM * 2>(sa, wr * 128, s, f.a);
     } else {
       const char* a_row0 = sa + (wr * 128 + r32) * ROWB;
 #pragma unroll
@@ -413,9 +452,9 @@ struct Slots {
   __device__ inline char* b(int i) const { return lds + 3 * Smem<BN>::kA + i * Smem<BN>::kB; }
 };
 
-template <typename T, int BN, int WC, bool kAT = false>
+template <typename T, int BN, int WC, bool kAT = false, bool kBT = false>
 struct KLoop {
-  using ML = MainLoop<T, BN, WC, kAT>;
+  using ML = MainLoop<T, BN, WC, kAT, kBT>;
   ML ml;
   Slots<BN> sl;
   int kb_full;
@@ -469,18 +508,18 @@ struct KLoop {
 
 // Forced inline: several kernels instantiate the same main loop and epilogue,
 // and an out-of-line call would pass the accumulators through scratch memory.
-template <typename T, int BN, int WC, bool kAT = false>
+template <typename T, int BN, int WC, bool kAT = false, bool kBT = false>
 __device__ __attribute__((always_inline)) inline void gemm_mainloop(const Operand& A, const Operand& B, int k_elems, int tm, int tn,
                                      int kb0, int kb1, char* lds,
                                      f32x16 (&acc)[4][BN / (32 * WC)]) {
-  using ML = MainLoop<T, BN, WC, kAT>;
+  using ML = MainLoop<T, BN, WC, kAT, kBT>;
 #pragma unroll
   for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
     for (int bj = 0; bj < ML::NBJ; ++bj)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[bi][bj][e] = 0.f;
-  KLoop<T, BN, WC, kAT> L;
+  KLoop<T, BN, WC, kAT, kBT> L;
   L.sl.lds = lds;
   L.ml.init(A, B, k_elems, tm, tn);
   L.kb_full = min(kb1, k_elems / ML::BK);  // blocks entirely inside the contraction
@@ -510,7 +549,7 @@ __device__ __attribute__((always_inline)) inline void gemm_mainloop(const Operan
   if (kb + 4 < kb_full) L.template step<4>(kb + 4, acc);
   wait_vmcnt<0>();      // the trailing out-of-range loads, before LDS is reused
   __syncthreads();
-  if (!kAT && kb_full < kb1) {  // ragged last block (at most one; never with k-major A)
+  if (!kAT && !kBT && kb_full < kb1) {  // ragged last block (at most one; never k-major)
     char* const sa = L.sl.a(0);
     char* const sb = L.sl.b(0);
     L.ml.load_ragged(kb_full, sa, sb);
@@ -896,7 +935,7 @@ constexpr int kPlainThreads = 128 * kPlainWC;
 // Tile walks of the plain GEMMs (measured per kernel).
 enum class Walk { kMSliced, kLinear };
 
-template <typename T, bool kAccumulate, Walk kWalk, bool kAT = false>
+template <typename T, bool kAccumulate, Walk kWalk, bool kAT = false, bool kBT = false>
 __device__ __attribute__((always_inline)) inline void plain_gemm(char* lds, Operand A, Operand B, int k_elems, int tiles_m,
                                   int tiles_n, int splits, int kb_per_split, float* out,
                                   long long ld_out, long long split_stride, int M, int N) {
@@ -907,7 +946,7 @@ __device__ __attribute__((always_inline)) inline void plain_gemm(char* lds, Oper
   const int kb0 = ti.split * kb_per_split;
   const int kb1 = min(kb0 + kb_per_split, kb_total);
   f32x16 acc[4][NBJ];
-  gemm_mainloop<T, BN, WC, kAT>(A, B, k_elems, ti.tm, ti.tn, kb0, kb1, lds, acc);
+  gemm_mainloop<T, BN, WC, kAT, kBT>(A, B, k_elems, ti.tm, ti.tn, kb0, kb1, lds, acc);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave / WC, wc = wave % WC, r32 = lane & 31, h = lane >> 5;
@@ -966,15 +1005,15 @@ __device__ __attribute__((always_inline)) inline void plain_gemm(char* lds, Oper
 
 // Distinct kernel names for dH (split-K partials, plain stores) and dW
 // (accumulated into the caller's fp32 dW).
-template <typename T>
+template <typename T, bool kBT>
 __global__ __launch_bounds__(kPlainThreads, 1) void dh_gemm_kernel(Operand A, Operand B, int k_elems,
                                                                     int tiles_m, int tiles_n, int splits,
                                                                     int kb_per_split, float* out,
                                                                     long long ld_out,
                                                                     long long split_stride, int M, int N) {
   KD_DECLARE_LDS(TILE_D);
-  plain_gemm<T, false, Walk::kMSliced>(lds, A, B, k_elems, tiles_m, tiles_n, splits, kb_per_split,
-                                       out, ld_out, split_stride, M, N);
+  plain_gemm<T, false, Walk::kMSliced, false, kBT>(lds, A, B, k_elems, tiles_m, tiles_n, splits,
+                                                   kb_per_split, out, ld_out, split_stride, M, N);
 }
 
 template <typename T, bool kAccumulate, bool kAT>
@@ -993,6 +1032,7 @@ Operand make_operand(const void* base, long long ld_elems, int rows) {
   o.base = static_cast<const char*>(base);
   o.ld = ld_elems * (long long)sizeof(T);
   o.rows = rows;
+  o.krows = 0;
   return o;
 }
 
@@ -1046,21 +1086,29 @@ void launch_recompute_gemm(DType t, const void* W, int V, const void* Hc, int ro
     recompute_impl<float>(W, V, Hc, rows, d, ep, s);
 }
 
-void launch_dh_gemm(DType t, const void* G, int rows, int v_pad, const void* WT, int d, int splits,
-                    float* part, long long split_stride, hipStream_t s) {
+void launch_dh_gemm(DType t, const void* G, int rows, int v_pad, const void* Wop, bool w_kmajor, int V,
+                    int d, int splits, float* part, long long split_stride, hipStream_t s) {
   const int tiles_m = (rows + BM - 1) / BM, tiles_n = (d + TILE_D - 1) / TILE_D;
   const int bk = k_block(t);
   const int kb_total = (v_pad + bk - 1) / bk;
   const int kb_per = (kb_total + splits - 1) / splits;
   const int grid = tiles_m * tiles_n * splits;
-  if (t == DType::BF16)
-    dh_gemm_kernel<__bf16><<<grid, kPlainThreads, 0, s>>>(
-        make_operand<__bf16>(G, v_pad, rows), make_operand<__bf16>(WT, v_pad, d), v_pad, tiles_m,
+  if (t == DType::BF16 && w_kmajor) {
+    // B = W itself, [V][d]: k-major, n extent d, V k rows (rows V .. v_pad read as zero)
+    Operand B = make_operand<__bf16>(Wop, d, d);
+    B.krows = V;
+    dh_gemm_kernel<__bf16, true><<<grid, kPlainThreads, 0, s>>>(
+        make_operand<__bf16>(G, v_pad, rows), B, v_pad, tiles_m, tiles_n, splits, kb_per, part, d,
+        split_stride, rows, d);
+  } else if (t == DType::BF16) {
+    dh_gemm_kernel<__bf16, false><<<grid, kPlainThreads, 0, s>>>(
+        make_operand<__bf16>(G, v_pad, rows), make_operand<__bf16>(Wop, v_pad, d), v_pad, tiles_m,
         tiles_n, splits, kb_per, part, d, split_stride, rows, d);
-  else
-    dh_gemm_kernel<float><<<grid, kPlainThreads, 0, s>>>(
-        make_operand<float>(G, v_pad, rows), make_operand<float>(WT, v_pad, d), v_pad, tiles_m,
+  } else {
+    dh_gemm_kernel<float, false><<<grid, kPlainThreads, 0, s>>>(
+        make_operand<float>(G, v_pad, rows), make_operand<float>(Wop, v_pad, d), v_pad, tiles_m,
         tiles_n, splits, kb_per, part, d, split_stride, rows, d);
+  }
 }
 
 template <typename T, bool kAcc, bool kAT>

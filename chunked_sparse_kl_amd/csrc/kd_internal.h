@@ -109,9 +109,11 @@ void launch_fwd_gemm(DType t, const void* W, int V, const void* Hc, int rows, in
 // Same contraction, epilogue: G = grad * w_t (S_t q - scatter p) into G and G^T.
 void launch_recompute_gemm(DType t, const void* W, int V, const void* Hc, int rows, int d,
                            const RecomputeEpilogue& ep, hipStream_t s);
-// part[split][c_pad][d] = G[:, split range] * W^T[split range, :]  (fp32 partials)
-void launch_dh_gemm(DType t, const void* G, int rows, int v_pad, const void* WT, int d,
-                    int splits, float* part, long long split_stride, hipStream_t s);
+// part[split][c_pad][d] = G[:, split range] * W[split range, :]  (fp32 partials).
+// w_kmajor (bf16 only): Wop is W itself, [V][d], read k-major through
+// transposing LDS reads; otherwise Wop is W^T, [d][v_pad] (rows V .. v_pad zero).
+void launch_dh_gemm(DType t, const void* G, int rows, int v_pad, const void* Wop, bool w_kmajor, int V,
+                    int d, int splits, float* part, long long split_stride, hipStream_t s);
 // dW[V][d] (+)= G^T * H over k_len token columns (G^T rows of pitch ld_gt,
 // H^T rows of pitch ld_ht); accumulate == false overwrites dW.
 void launch_dw_gemm(DType t, const void* GT, int V, int k_len, long long ld_gt, const void* HT, int d,
