@@ -1,16 +1,19 @@
 // MFMA GEMM core of kdloss (gfx950) and its four epilogues.
 //
 // Every contraction of the path is written as  D[m][n] = sum_k A[m][k] * B[n][k]
-// with both operands stored K-contiguous ("NT"), so one main loop serves all:
+// with the operands K-contiguous ("NT") or, for bf16, read k-major through
+// transposing LDS reads, so one main loop serves all:
 //   forward / recompute:  A = W [V][d],      B = H_c [C][d]     (D = logits^T)
-//   dH:                   A = G [C][V],      B = W^T [d][V]     (split over V)
-//   dW:                   A = G^T [V][C],    B = H_c^T [d][C]
+//   dH:                   A = G [C][V],      B = W [V][d] k-major (bf16) or
+//                                            W^T [d][V] (fp32)  (split over V)
+//   dW:                   A = G [2C][V] k-major (bf16) or G^T [V][2C] (fp32),
+//                         B = H_c^T [d][2C]                     (pairs of chunks)
 // A 512-thread workgroup (8 wavefronts in a 2 x 4 grid, two per SIMD) owns a
 // 256 x 256 tile; each wavefront owns 128 x 64 and accumulates it in 32x32
 // MFMA blocks (v_mfma_f32_32x32x16_bf16 for bf16, v_mfma_f32_32x32x2f32 for
-// fp32).  The K loop stages 128-byte rows of A and B (one K block) through
-// LDS with direct-to-LDS loads into two stages: block kb+1 lands while kb is
-// multiplied, and kb+2 is issued during kb's last substep.
+// fp32).  The K loop stages 128 bytes of K per row of A and B (one K block)
+// through LDS with direct-to-LDS loads into three A and two B slots: A is
+// loaded two blocks ahead and B one block ahead of the block multiplied.
 //
 // Accumulator layout of one 32x32 block (lane l, register e = 4*i + j):
 //   row  = 8*i + 4*(l / 32) + j,   column = l % 32.
@@ -130,7 +133,7 @@ __device__ inline TileIdx map_tile(int tiles_m, int tiles_n, int splits) {
 //    (dW: every XCD reads the same rows of G at about the same time);
 //  * M-sliced (tiles_m % 8 == 0, else the XCD ranges above): XCD x owns the
 //    M tiles [x * tiles_m / 8, ...) and all XCDs walk the N tiles (then the
-//    splits) in step (dH: every XCD reads the same W^T tiles).
+//    splits) in step (dH: every XCD reads the same W tiles).
 template <int kGroupM>
 __device__ inline TileIdx map_tile_linear(int tiles_m, int tiles_n, int splits) {
   const int lin = blockIdx.x;
@@ -762,9 +765,9 @@ __global__ __launch_bounds__(kFusedThreads, 1) void fwd_gemm_kernel(Operand A, O
 // with q = softmax(z / tau) and gw = tau * grad_loss * mask_t / N_valid (the
 // derivative of tau^2 KL through z / tau), formed in the accumulators (the
 // scatter goes straight into the owning registers), rounded to T and written
-// transposed (G^T, straight from registers: a lane's 32-token column is
-// contiguous there) and row-major (G, through a per-wavefront LDS block so the
-// stores are whole rows).
+// row-major (G, through a per-wavefront LDS block so the stores are whole
+// rows) and, for fp32 only, transposed (G^T, straight from registers: a
+// lane's 32-token column is contiguous there).
 template <typename T>
 __global__ __launch_bounds__(kFusedThreads, 1) void recompute_gemm_kernel(Operand A, Operand B,
                                                                            int k_elems, int tiles_m,
@@ -817,42 +820,25 @@ __global__ __launch_bounds__(kFusedThreads, 1) void recompute_gemm_kernel(Operan
   });
 
   T* G = static_cast<T*>(ep.G);
-  T* GT = static_cast<T*>(ep.GT);
-  // --- G^T[v][n] (only when the dW GEMM reads G^T rather than G itself): for
-  // a fixed register, the 32 lanes of a half-wavefront
-  // hold 32 consecutive tokens of one vocabulary row.  bf16: neighbouring
-  // lanes swap values so each lane stores two tokens (4 bytes).
-  if (GT != nullptr) {
+  // --- G^T[v][n] (fp32 only: the bf16 dW GEMM reads G itself k-major): for
+  // a fixed register, the 32 lanes of a half-wavefront hold 32 consecutive
+  // tokens of one vocabulary row.
+  if constexpr (sizeof(T) == 4) {
+    T* GT = static_cast<T*>(ep.GT);
 #pragma unroll
-  for (int bi = 0; bi < 4; ++bi)
+    for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-    for (int bj = 0; bj < NBJ; ++bj) {
-      const int n = n_wave + bj * 32 + r32;
+      for (int bj = 0; bj < NBJ; ++bj) {
+        const int n = n_wave + bj * 32 + r32;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int v0 = v_wave + bi * 32 + 8 * i + 4 * h;
-        if constexpr (sizeof(T) == 2) {
-#pragma unroll
-          for (int jp = 0; jp < 2; ++jp) {
-            const float x0 = acc[bi][bj][4 * i + 2 * jp], x1 = acc[bi][bj][4 * i + 2 * jp + 1];
-            const float y0 = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x0), 0xB1, 0xF, 0xF, true));
-            const float y1 = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x1), 0xB1, 0xF, 0xF, true));
-            const bool odd = (lane & 1) != 0;
-            const int v = v0 + 2 * jp + (odd ? 1 : 0);
-            const int n2 = n & ~1;
-            T pr[2] = {(T)(odd ? y1 : x0), (T)(odd ? x1 : y0)};
-            if (v < ep.v_pad && n2 < ep.c_pad)
-              __builtin_nontemporal_store(*reinterpret_cast<const uint32_t*>(pr),
-                                          reinterpret_cast<uint32_t*>(GT + (long long)v * ep.gt_ld + ep.gt_col0 + n2));
-          }
-        } else {
+        for (int i = 0; i < 4; ++i) {
+          const int v0 = v_wave + bi * 32 + 8 * i + 4 * h;
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             if (v0 + j < ep.v_pad && n < ep.c_pad)
               __builtin_nontemporal_store((T)acc[bi][bj][4 * i + j], GT + (long long)(v0 + j) * ep.gt_ld + ep.gt_col0 + n);
         }
       }
-    }
   }
   // --- G[n][v]: each wavefront stages its 32-token x 128-row blocks (rounded
   // to T) in its own LDS rows and stores whole 128-value rows.

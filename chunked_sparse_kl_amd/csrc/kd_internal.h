@@ -80,7 +80,7 @@ struct FwdEpilogue {
 
 struct RecomputeEpilogue {
   void* G;             // [*][v_pad] dtype; this chunk's rows start at g_row0
-  void* GT;            // [v_pad][gt_ld] dtype or null; this chunk's columns start at gt_col0
+  void* GT;            // fp32 only: [v_pad][gt_ld]; this chunk's columns start at gt_col0 (bf16: unused)
   int g_row0;
   int gt_ld;
   int gt_col0;

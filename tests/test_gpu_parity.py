@@ -42,8 +42,8 @@ def test_small_ragged(dtype, chunk):
 @pytest.mark.parametrize("d", [320, 288])
 def test_narrow_last_column_tile(dtype, d):
     # d = 256 + 64 / 256 + 32: the dH and dW tiles of the last 256 hidden
-    # columns take the narrow (64-column) tile path; 4 chunks, so dW is
-    # written by the first pair and accumulated by the second
+    # columns hold only 64 / 32 valid columns; 4 chunks, so dW is written by
+    # the first pair and accumulated by the second
     inp = synth.make_custom(700, d, 1100, 24, dtype, "random5", "uniform", seed=25)
     gpu = run_gpu(inp, chunk=192, grad=1.3)
     assert gpu["plan"]["n_chunks"] == 4
