@@ -372,11 +372,12 @@ struct MainLoop {
     const int lane = threadIdx.x & 63;
     const int g = lane >> 4, q = lane & 15, x = q >> 2;
     const int m = idx0 + 16 * (g & 1) + 4 * (q & 3);
-    const unsigned base = lds_addr(slot) + (unsigned)((8 * (g >> 1) + x) * kRowBytes + (m & 7) * 2);
     typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) char lds_char;
+    lds_char* const base = (lds_char*)const_cast<char*>(slot) + ((8 * (g >> 1) + x) * kRowBytes + (m & 7) * 2);
 #pragma unroll
     for (int bi = 0; bi < NBLK; ++bi) {
-      const unsigned a = base + ((((m >> 3) + 4 * bi) ^ (4 * x)) << 4);
+      lds_char* const a = base + ((((m >> 3) + 4 * bi) ^ (4 * x)) << 4);
       const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) v4s*)(a + (16 * s) * kRowBytes));
       const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
