@@ -50,6 +50,16 @@ def test_narrow_last_column_tile(dtype, d):
     check_full(inp, gpu, dtype, grad=1.3)
 
 
+@pytest.mark.parametrize("dtype,n,d,V,K", [("bf16", 70, 40, 100, 7), ("f32", 33, 12, 50, 50),
+                                           ("bf16", 5, 8, 300, 3)])
+def test_below_one_tile_and_one_k_block(dtype, n, d, V, K):
+    # d below one 64-wide K block (only the ragged block runs), V below or just
+    # over one 256-wide vocabulary tile, n below one 256-row tile
+    inp = synth.make_custom(n, d, V, K, dtype, "random5", "uniform", seed=26)
+    gpu = run_gpu(inp, chunk=0)
+    check_full(inp, gpu, dtype)
+
+
 def test_tiny_fp32_workload_full():
     inp = synth.make_inputs(1)
     gpu = run_gpu(inp, chunk=inp["workload"].chunk)

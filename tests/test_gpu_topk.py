@@ -70,6 +70,14 @@ def test_small_ragged(dtype, V, K):
     _check(Ht, Wt, K, idx, logp)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_below_one_tile_and_one_k_block(dtype):
+    # d = 40: only the ragged K block; V = 100: one partial vocabulary tile (< K tiles: no threshold)
+    Ht, Wt = _inputs(70, 40, 100, dtype, seed=37)
+    idx, logp = _run(Ht, Wt, 7)
+    _check(Ht, Wt, 7, idx, logp)
+
+
 def test_k_equals_v():
     Ht, Wt = _inputs(130, 64, 300, "bf16", seed=32)
     idx, logp = _run(Ht, Wt, 300, chunk=64)
