@@ -24,6 +24,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "fused chunked KL fwd+bwd tokens/s & TFLOP/s (% bf16 MFMA peak); peak GiB"
 BF16_PEAK_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 dense bf16 flop/clk/CU
+FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X published dense fp32 matrix rate
 HBM_PEAK_GBS = 8000.0
 WORKLOAD = 4                # 32K tokens, d=2880, V=201088, K=100
 
@@ -32,13 +33,16 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_traffic(kernel: str):
+def kernel_traffic(kernel: str, workload: str = None):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source (otherwise None)."""
+    was taken on the current kernel source and on `workload` (a workload name
+    followed by the chunk, as the record states it; otherwise None)."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
+    if workload is not None and rec.get("workload") != workload:
+        return None
     src = open(os.path.join(ROOT, "chunked_sparse_kl_amd", "csrc", rec["source_file"]), "rb").read()
     if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
         return None
@@ -72,14 +76,16 @@ def cpu_baseline(inp: dict, rows: int, seed: int = 3) -> dict:
                       f"{dt:.1f} s wall"}
 
 
-def roofline_of(stats: list, kernel_traffic_fn) -> dict:
-    """Roofline record of the kernel with the largest summed time."""
+def roofline_of(stats: list, kernel_traffic_fn, mfma_peak: float = None) -> dict:
+    """Roofline record of the kernel with the largest summed time; contractions
+    are priced against the MFMA peak of their dtype (bf16 unless given)."""
+    peak = BF16_PEAK_TFLOPS if mfma_peak is None else mfma_peak
     dom = max(stats, key=lambda s: s["total_ms"])
     avg_ms = dom["total_ms"] / dom["launches"]
     if dom["flops"] > 0:
         achieved = dom["flops"] / dom["launches"] / (avg_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
     else:
         achieved = dom["bytes"] / dom["launches"] / (avg_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -206,6 +212,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--workload", type=int, default=WORKLOAD, choices=sorted((1, 2, 3, 4, 5)),
+                    help="1 tiny fp32, 2 toy-head 4K, 3 packed 8K, 4 head-32K (the headline), 5 long 256K")
     ap.add_argument("--cpu-rows", type=int, default=2048, help="rows of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -240,13 +248,14 @@ def main() -> int:
     from chunked_sparse_kl_amd import synth
 
     dev = torch.device("cuda", 0)
-    w = synth.WORKLOADS[WORKLOAD]
+    w = synth.WORKLOADS[args.workload]
     log(f"generating inputs: {w.name}")
-    inp = synth.make_inputs(WORKLOAD)
+    inp = synth.make_inputs(args.workload)
     H, W = inp["H"].to(dev), inp["W"].to(dev)
     idx, logp, mask = inp["idx"].to(dev), inp["logp"].to(dev), inp["mask"].to(dev)
     T, d, V, K = w.T, w.d, w.V, w.K
-    plan = kd.kd_plan_query(kd.KD_BF16, T, d, V, K, args.chunk)
+    dtype = kd.KD_BF16 if w.dtype == "bf16" else kd.KD_F32
+    plan = kd.kd_plan_query(dtype, T, d, V, K, args.chunk if args.chunk else w.chunk)
     log(f"plan: {plan}")
     ws = torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device=dev)
     dW = torch.empty((V, d), dtype=torch.float32, device=dev)
@@ -287,7 +296,9 @@ def main() -> int:
         log(f"  {s['name']:16s} launches={s['launches']:4d} total={s['total_ms']:9.3f} ms "
             f"avg={s['total_ms'] / s['launches']:8.3f} ms "
             f"{(s['flops'] / (s['total_ms'] * 1e-3) / 1e12) if s['flops'] else 0:8.1f} TFLOP/s")
-    roof = roofline_of(stats, kernel_traffic)
+    run_name = f"{w.name} chunk {plan['chunk']}"
+    roof = roofline_of(stats, lambda k: kernel_traffic(k, run_name),
+                       BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -299,7 +310,7 @@ def main() -> int:
     out = {
         "metric": METRIC, "value": round(tokens_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "T": T, "d": d, "V": V, "K": K, "mask": w.mask,
                    "chunk": plan["chunk"], "n_chunks": plan["n_chunks"],
