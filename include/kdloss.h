@@ -76,8 +76,8 @@ typedef struct kd_plan {
 
 /*
  * Chooses the chunk size and reports the workspace each call needs.  The
- * chunk bounds the only per-chunk buffers (the bf16/fp32 logit-gradient
- * slices G and G^T of chunk x V entries); everything else is linear in n.
+ * chunk bounds the only per-chunk buffers (the logit-gradient slices of
+ * chunk x V entries: G, and for fp32 also G^T); everything else is linear in n.
  * chunk > 0 is honoured as given (it must be a multiple of 64 unless it is
  * >= n).  chunk <= 0 lets the planner pick the largest multiple of 256 that is
  * <= 8192, <= max(256, n/2 rounded up to 256) and whose workspace fits in
