@@ -372,3 +372,86 @@ def test_padding_entries_equal_zero_probability_entries():
         gb = O.backward(H, W, idx, ref_logp, mask, temperature=tau)
         np.testing.assert_allclose(ga["dW"], gb["dW"], rtol=1e-12, atol=1e-16)
         np.testing.assert_allclose(ga["dH"], gb["dH"], rtol=1e-12, atol=1e-16)
+
+
+# ---------------------------------------------------------------- exact upcast of the storage dtypes
+def _bf16_from_words(words: np.ndarray) -> torch.Tensor:
+    """A torch bfloat16 tensor holding exactly the given 16-bit patterns."""
+    return torch.from_numpy(words.astype(np.uint16).view(np.int16).copy()).view(torch.bfloat16)
+
+
+def _decode_bf16_words(words: np.ndarray) -> np.ndarray:
+    """Hand decode: a bf16 word is the upper half of an IEEE binary32 word."""
+    return (words.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _bf16_words_of(values) -> np.ndarray:
+    """The bf16 patterns of float32 values that bf16 holds exactly (upper halves)."""
+    w = np.asarray(values, dtype=np.float32).view(np.uint32)
+    assert ((w & 0xFFFF) == 0).all(), "value not representable in bf16"
+    return (w >> 16).astype(np.uint16)
+
+
+def _upcast_case(seed=41):
+    """bf16 H and W whose entries a half-precision round trip would change:
+    magnitudes above 65504 (fp16 overflows to inf), below 6.1e-5 (fp16
+    subnormal or zero), and full 8-bit significands (1 + m/128)."""
+    rng = np.random.default_rng(seed)
+    T, d, V, K = 7, 8, 24, 5
+    sig = 1.0 + rng.integers(0, 128, size=(T, d)) / 128.0               # 8-bit significands
+    H = sig * np.exp2(rng.integers(-3, 3, size=(T, d))) * rng.choice([-1.0, 1.0], size=(T, d))
+    H[:, 0] = np.array([69632.0, -98304.0, 131072.0, 65536.0, -73728.0, 262144.0, 99328.0])  # > 65504
+    Wv = (1.0 + rng.integers(0, 128, size=(V, d)) / 128.0) * np.exp2(rng.integers(-4, 0, size=(V, d)))
+    Wv *= rng.choice([-1.0, 1.0], size=(V, d))
+    Wv[:, 0] = (1.0 + rng.integers(0, 128, size=V) / 128.0) * np.exp2(-rng.integers(18, 24, size=V))  # < 6.1e-5
+    Wv[:, 0] *= rng.choice([-1.0, 1.0], size=V)
+    Hw = _bf16_words_of(H.astype(np.float32))
+    Ww = _bf16_words_of(Wv.astype(np.float32))
+    idx = np.stack([rng.permutation(V)[:K] for _ in range(T)]).astype(np.int32)
+    logp = rng.standard_normal((T, K))
+    mask = np.ones(T, dtype=np.uint8)
+    mask[3] = 0
+    return Hw, Ww, idx, logp, mask
+
+
+def test_bf16_words_are_outside_half_precision():
+    # the case really exercises what a half-precision round trip would lose
+    Hw, Ww, *_ = _upcast_case()
+    Hb, Wb = _bf16_from_words(Hw), _bf16_from_words(Ww)
+    assert not torch.equal(Hb.float().half().float(), Hb.float())   # overflow above 65504
+    assert not torch.equal(Wb.float().half().float(), Wb.float())   # subnormal / flushed below 6.1e-5
+
+
+def test_to_f64_decodes_bf16_words_exactly():
+    Hw, Ww, *_ = _upcast_case()
+    for words in (Hw, Ww):
+        got = O.to_f64(_bf16_from_words(words))
+        want = _decode_bf16_words(words)
+        assert got.dtype == np.float64 and np.array_equal(got, want)
+        assert np.array_equal(got, _bf16_from_words(words).to(torch.float64).numpy())
+
+
+def test_forward_and_backward_on_bf16_tensors_equal_the_decoded_values():
+    """The oracle's bf16 entry (torch tensors straight from storage) gives
+    exactly the results of the hand-decoded fp64 values."""
+    Hw, Ww, idx, logp, mask = _upcast_case()
+    Hb, Wb = _bf16_from_words(Hw), _bf16_from_words(Ww)
+    Hd, Wd = _decode_bf16_words(Hw), _decode_bf16_words(Ww)
+    lp32 = torch.from_numpy(logp.astype(np.float32))
+    fa = O.forward(Hb, Wb, idx, lp32, mask)
+    fb = O.forward(Hd, Wd, idx, logp.astype(np.float32).astype(np.float64), mask)
+    assert np.isfinite(fa["loss"]) and fa["loss"] == fb["loss"]
+    assert np.array_equal(fa["lse"], fb["lse"]) and np.array_equal(fa["row_kl"], fb["row_kl"])
+    ba = O.backward(Hb, Wb, idx, lp32, mask, grad_loss=0.9)
+    bb = O.backward(Hd, Wd, idx, logp.astype(np.float32).astype(np.float64), mask, grad_loss=0.9)
+    assert np.isfinite(ba["dW"]).all() and np.array_equal(ba["dH"], bb["dH"])
+    assert np.array_equal(ba["dW"], bb["dW"])
+    # and the decoded values are not what fp16 storage would have given
+    Hh = torch.from_numpy(Hd.astype(np.float32)).half().double().numpy()
+    assert not np.isfinite(Hh).all()
+
+
+def test_to_f64_of_fp32_tensors_and_arrays_is_exact():
+    x = np.array([1.0 + 2.0 ** -23, 3.0e38, 1.0e-45, -7.25e-39], dtype=np.float32)
+    assert np.array_equal(O.to_f64(torch.from_numpy(x)), x.astype(np.float64))
+    assert np.array_equal(O.to_f64(x), x.astype(np.float64))
