@@ -49,31 +49,67 @@ def kernel_traffic(kernel: str, workload: str = None):
     return rec["hbm_bytes_per_launch"]
 
 
+def host_cpus() -> tuple:
+    """(CPUs this process may run on, threads the oracle is given): the
+    affinity set, capped by OMP_NUM_THREADS when the host sets a share."""
+    cpus = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    threads = min(cpus, int(omp)) if omp.isdigit() and int(omp) > 0 else cpus
+    return cpus, threads
+
+
 def blas_threads() -> int:
-    """Threads of the host BLAS the oracle's matrix products run on."""
-    try:
-        from threadpoolctl import threadpool_info
-        return max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
-    except Exception:  # pragma: no cover
-        return os.cpu_count() or 1
+    """Threads of the host BLAS the oracle's matrix products run on now."""
+    from threadpoolctl import threadpool_info
+    return max((p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"),
+               default=1)
+
+
+def timed_oracle(fn):
+    """Runs fn() with the host BLAS on the threads host_cpus() grants; returns
+    (result, seconds, threads used, CPUs visible)."""
+    from threadpoolctl import threadpool_limits
+    cpus, threads = host_cpus()
+    with threadpool_limits(limits=threads, user_api="blas"):
+        used = blas_threads()
+        t0 = time.perf_counter()
+        out = fn()
+        dt = time.perf_counter() - t0
+    return out, dt, used, cpus
 
 
 def cpu_baseline(inp: dict, rows: int, seed: int = 3) -> dict:
-    """The CPU fp64 oracle, as it stands, on a seeded subset of rows (forward and
-    backward of those rows)."""
+    """The CPU fp64 oracle (numpy, oracle/kl_oracle.py), as it stands, on a
+    seeded subset of rows (forward and backward of those rows), on the host's
+    cores."""
     from oracle import kl_oracle as O
-    threads = blas_threads()
     n = inp["H"].shape[0]
     S = np.sort(np.random.default_rng(seed).choice(n, size=rows, replace=False))
     mask = inp["mask"].numpy()
-    t0 = time.perf_counter()
-    f = O.forward(inp["H"], inp["W"], inp["idx"].numpy(), inp["logp"], mask, rows=S)
-    b = O.backward(inp["H"], inp["W"], inp["idx"].numpy(), inp["logp"], mask, rows=S)
-    dt = time.perf_counter() - t0
+
+    def run():
+        f = O.forward(inp["H"], inp["W"], inp["idx"].numpy(), inp["logp"], mask, rows=S)
+        b = O.backward(inp["H"], inp["W"], inp["idx"].numpy(), inp["logp"], mask, rows=S)
+        return f, b
+
+    (f, b), dt, used, cpus = timed_oracle(run)
     assert np.isfinite(f["loss"]) and np.isfinite(b["dW"]).all()
-    return {"value": rows / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{rows} seeded rows of the same workload, forward + backward, fp64, "
-                      f"{dt:.1f} s wall"}
+    return {"value": rows / dt, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
+            "host_cpus": int(cpus),
+            "sample": f"numpy fp64 oracle, BLAS on {used} threads of {cpus} visible CPUs; "
+                      f"{rows} seeded rows of the same workload, forward + backward, {dt:.1f} s wall"}
+
+
+def make_step(kd, H, W, idx, logp, mask, plan, ws, dW, grad):
+    """One timed step: the forward call, then the backward call on the same
+    workspace, overwriting dW (accumulate=False: every element written, none
+    read).  Returns a function giving (loss, dH) of one step."""
+    def step():
+        fw = kd.kd_fused_chunked_kl_fwd(H, W, idx, logp, mask, workspace=ws, row_kl=False, plan=plan)
+        dH, _ = kd.kd_fused_chunked_kl_bwd(H, W, idx, logp, mask, fw["lse"], grad, workspace=ws,
+                                           dW=dW, plan=plan, accumulate=False)
+        return fw["loss"], dH
+    return step
 
 
 def roofline_of(stats: list, kernel_traffic_fn, mfma_peak: float = None) -> dict:
@@ -134,13 +170,12 @@ def topk_builder_main(args) -> int:
     if not args.no_cpu_baseline:
         from oracle import topk_cache_oracle as TO
         rows = np.sort(np.random.default_rng(3).choice(T, size=args.cpu_rows_topk, replace=False))
-        t0 = time.perf_counter()
-        ref = TO.build_cache(inp["H"], inp["W"], K, rows=rows)
-        dt = time.perf_counter() - t0
+        ref, dt, used, cpus = timed_oracle(lambda: TO.build_cache(inp["H"], inp["W"], K, rows=rows))
         assert (ref["logp"] <= 0).all()
-        cpu = {"value": rows.size / dt, "unit": "tokens/s", "cores": blas_threads(),
-               "kind": "oracle", "sample": f"{rows.size} seeded rows of the same shape, fp64, "
-                                           f"{dt:.1f} s wall"}
+        cpu = {"value": rows.size / dt, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
+               "host_cpus": int(cpus),
+               "sample": f"numpy fp64 cache-builder oracle, BLAS on {used} threads of {cpus} visible "
+                         f"CPUs; {rows.size} seeded rows of the same shape, {dt:.1f} s wall"}
         log(f"cpu baseline: {cpu}")
     out = {
         "metric": "teacher top-K cache build tokens/s", "value": round(T * args.steps / elapsed, 1),
@@ -262,11 +297,7 @@ def main() -> int:
     grad = torch.ones(1, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
-    def step():
-        fw = kd.kd_fused_chunked_kl_fwd(H, W, idx, logp, mask, workspace=ws, row_kl=False, plan=plan)
-        dH, _ = kd.kd_fused_chunked_kl_bwd(H, W, idx, logp, mask, fw["lse"], grad, workspace=ws,
-                                           dW=dW, plan=plan, accumulate=False)
-        return fw["loss"], dH
+    step = make_step(kd, H, W, idx, logp, mask, plan, ws, dW, grad)
 
     for i in range(args.warmup):
         loss, _ = step()

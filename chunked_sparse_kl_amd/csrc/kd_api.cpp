@@ -247,8 +247,18 @@ int resolve_chunk(int64_t n, int64_t chunk, int64_t* out) {
   return KD_OK;
 }
 
+// Which workspace the automatic chunk must fit: both calls' (the planner
+// query: one buffer can serve both), or only the forward's / backward's (the
+// loss calls given chunk <= 0 plan against the buffer they are handed; loss
+// and LSE do not depend on the chunk, so the two calls may choose differently).
+enum class Fit { kBoth, kFwd, kBwd };
+
+size_t fit_bytes(const Layout& L, Fit f) {
+  return f == Fit::kFwd ? L.fwd_end : f == Fit::kBwd ? L.bwd_end : std::max(L.fwd_end, L.bwd_end);
+}
+
 int plan(int dtype, int64_t n, int64_t d, int64_t V, int64_t K, int64_t chunk, size_t budget_in,
-         Layout* out) {
+         Layout* out, Fit fit = Fit::kBoth) {
   int rc = check_sizes(dtype, n, d, V, K);
   if (rc != KD_OK) return rc;
   int64_t c = 0;
@@ -269,9 +279,9 @@ int plan(int dtype, int64_t n, int64_t d, int64_t V, int64_t K, int64_t chunk, s
   budget = std::min(budget, kWorkspaceCap);
   if (n <= 256) {
     Layout L = make_layout(dt, n, d, V, K, n);
-    if (std::max(L.fwd_end, L.bwd_end) > budget)
+    if (fit_bytes(L, fit) > budget)
       return fail(KD_E_WORKSPACE, "workspace of %zu bytes exceeds the budget of %zu bytes",
-                  std::max(L.fwd_end, L.bwd_end), budget);
+                  fit_bytes(L, fit), budget);
     *out = L;
     return KD_OK;
   }
@@ -280,14 +290,14 @@ int plan(int dtype, int64_t n, int64_t d, int64_t V, int64_t K, int64_t chunk, s
   for (int64_t cand = c_max; cand >= 256; cand -= 256) {
     const int64_t cc = std::min(cand, n);
     Layout L = make_layout(dt, n, d, V, K, cc);
-    if (std::max(L.fwd_end, L.bwd_end) <= budget) {
+    if (fit_bytes(L, fit) <= budget) {
       *out = L;
       return KD_OK;
     }
   }
   Layout L = make_layout(dt, n, d, V, K, std::min<int64_t>(256, n));
   return fail(KD_E_WORKSPACE, "no chunk size fits: the smallest plan (chunk 256) needs %zu bytes, budget %zu",
-              std::max(L.fwd_end, L.bwd_end), budget);
+              fit_bytes(L, fit), budget);
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -493,12 +503,10 @@ int kd_fused_chunked_kl_fwd(int dtype, const void* H, const void* W, const int32
                             void* workspace, size_t workspace_bytes, float* loss, float* lse,
                             float* row_kl, float* gathered, void* stream) {
   Layout L;
-  int rc = plan(dtype, n, d, V, K, chunk, workspace_bytes ? workspace_bytes : 1, &L);
-  if (rc != KD_OK && rc != KD_E_WORKSPACE) return rc;
-  if (rc == KD_E_WORKSPACE) {
-    // auto chunk with an undersized buffer: report what the smallest plan needs
-    return rc;
-  }
+  // chunk <= 0: the largest automatic chunk whose forward workspace fits the
+  // buffer given (an undersized buffer reports what the smallest plan needs)
+  int rc = plan(dtype, n, d, V, K, chunk, workspace_bytes ? workspace_bytes : 1, &L, Fit::kFwd);
+  if (rc != KD_OK) return rc;
   if (loss == nullptr || lse == nullptr) return fail(KD_E_INVAL, "loss and lse must be non-null");
   rc = check_temperature(temperature);
   if (rc != KD_OK) return rc;
@@ -551,7 +559,7 @@ int kd_fused_chunked_kl_bwd(int dtype, const void* H, const void* W, const int32
                             int accumulate_dw,
                             void* workspace, size_t workspace_bytes, void* stream) {
   Layout L;
-  int rc = plan(dtype, n, d, V, K, chunk, workspace_bytes ? workspace_bytes : 1, &L);
+  int rc = plan(dtype, n, d, V, K, chunk, workspace_bytes ? workspace_bytes : 1, &L, Fit::kBwd);
   if (rc != KD_OK) return rc;
   if (lse == nullptr || grad_loss == nullptr || dH == nullptr || dW == nullptr)
     return fail(KD_E_INVAL, "lse, grad_loss, dH and dW must be non-null");
@@ -611,12 +619,18 @@ int kd_fused_chunked_kl_bwd(int dtype, const void* H, const void* W, const int32
               double(L.V) * L.d * es + double(rows) * L.d * es + 2.0 * c_pad * L.v_pad * es,
               kd::launch_recompute_gemm(L.dt, W, (int)L.V, Hc, rows, (int)L.d, ep, s));
     const long long split_stride = (long long)L.c_pad * L.d;
+    const size_t dhpart_bytes = L.bwd_end - L.dhpart;
+    if (const char* why = kd::dh_launch_error(L.dt, rows, (int)L.v_pad, (int)L.d, (int)L.splits,
+                                              split_stride, dhpart_bytes))
+      return fail(KD_E_INVAL, "dH launch refused (%d splits, %d rows): %s", (int)L.splits, rows, why);
+    bool launched = false;
     KD_LAUNCH("dh_gemm", fl,
               double(c_pad) * L.v_pad * es + double(L.d) * L.v_pad * es + double(L.splits) * rows * L.d * 4,
-              kd::launch_dh_gemm(L.dt, ws + L.G + size_t(g_row0) * L.v_pad * es, rows, (int)L.v_pad,
-                                 w_kmajor ? W : ws + L.WT, w_kmajor, (int)L.V, (int)L.d,
-                                 (int)L.splits, reinterpret_cast<float*>(ws + L.dhpart),
-                                 split_stride, s));
+              launched = kd::launch_dh_gemm(L.dt, ws + L.G + size_t(g_row0) * L.v_pad * es, rows,
+                                            (int)L.v_pad, w_kmajor ? W : ws + L.WT, w_kmajor, (int)L.V,
+                                            (int)L.d, (int)L.splits, reinterpret_cast<float*>(ws + L.dhpart),
+                                            split_stride, dhpart_bytes, s));
+    if (!launched) return fail(KD_E_INVAL, "dH launch refused by its bounds check");
     KD_LAUNCH("dh_reduce", 0, double(L.splits) * rows * L.d * 4 + double(rows) * L.d * es,
               kd::launch_dh_reduce(L.dt, reinterpret_cast<const float*>(ws + L.dhpart),
                                    (int)L.splits, split_stride, rows, (int)L.d,

@@ -1073,8 +1073,25 @@ void launch_recompute_gemm(DType t, const void* W, int V, const void* Hc, int ro
     recompute_impl<float>(W, V, Hc, rows, d, ep, s);
 }
 
-void launch_dh_gemm(DType t, const void* G, int rows, int v_pad, const void* Wop, bool w_kmajor, int V,
-                    int d, int splits, float* part, long long split_stride, hipStream_t s) {
+const char* dh_launch_error(DType t, int rows, int v_pad, int d, int splits, long long split_stride,
+                            size_t part_bytes) {
+  if (rows <= 0 || v_pad <= 0 || d <= 0) return "empty operand";
+  if (splits < 1) return "splits must be at least 1";
+  const long long bk = k_block(t);
+  const long long kb_total = (v_pad + bk - 1) / bk;
+  if (splits > kb_total) return "more splits than K blocks in the contraction";
+  const long long kb_per = (kb_total + splits - 1) / splits;
+  if ((splits - 1) * kb_per >= kb_total) return "a split would hold no K block";
+  if ((long long)rows * d > split_stride) return "one split's partial exceeds the split stride";
+  if ((unsigned long long)splits * (unsigned long long)split_stride * 4ull > part_bytes)
+    return "the partials of all splits exceed the partials buffer";
+  return nullptr;
+}
+
+bool launch_dh_gemm(DType t, const void* G, int rows, int v_pad, const void* Wop, bool w_kmajor, int V,
+                    int d, int splits, float* part, long long split_stride, size_t part_bytes,
+                    hipStream_t s) {
+  if (dh_launch_error(t, rows, v_pad, d, splits, split_stride, part_bytes) != nullptr) return false;
   const int tiles_m = (rows + BM - 1) / BM, tiles_n = (d + TILE_D - 1) / TILE_D;
   const int bk = k_block(t);
   const int kb_total = (v_pad + bk - 1) / bk;
@@ -1096,6 +1113,7 @@ void launch_dh_gemm(DType t, const void* G, int rows, int v_pad, const void* Wop
         make_operand<float>(G, v_pad, rows), make_operand<float>(Wop, v_pad, d), v_pad, tiles_m,
         tiles_n, splits, kb_per, part, d, split_stride, rows, d);
   }
+  return true;
 }
 
 template <typename T, bool kAcc, bool kAT>

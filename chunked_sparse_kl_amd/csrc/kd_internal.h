@@ -112,8 +112,17 @@ void launch_recompute_gemm(DType t, const void* W, int V, const void* Hc, int ro
 // part[split][c_pad][d] = G[:, split range] * W[split range, :]  (fp32 partials).
 // w_kmajor (bf16 only): Wop is W itself, [V][d], read k-major through
 // transposing LDS reads; otherwise Wop is W^T, [d][v_pad] (rows V .. v_pad zero).
-void launch_dh_gemm(DType t, const void* G, int rows, int v_pad, const void* Wop, bool w_kmajor, int V,
-                    int d, int splits, float* part, long long split_stride, hipStream_t s);
+// The launch is refused (false, nothing launched) unless dh_launch_error
+// finds it in bounds for a partials buffer of part_bytes.
+bool launch_dh_gemm(DType t, const void* G, int rows, int v_pad, const void* Wop, bool w_kmajor, int V,
+                    int d, int splits, float* part, long long split_stride, size_t part_bytes,
+                    hipStream_t s);
+// nullptr if a dH launch stays inside its contraction and its partials
+// buffer: 1 <= splits, every split holds at least one K block of the v_pad
+// contraction, one split's partial (rows x d fp32) fits in split_stride
+// floats, and splits * split_stride floats fit in part_bytes; else the reason.
+const char* dh_launch_error(DType t, int rows, int v_pad, int d, int splits, long long split_stride,
+                            size_t part_bytes);
 // dW[V][d] (+)= G^T * H over k_len token columns (G^T rows of pitch ld_gt,
 // H^T rows of pitch ld_ht); accumulate == false overwrites dW.
 void launch_dw_gemm(DType t, const void* GT, int V, int k_len, long long ld_gt, const void* HT, int d,

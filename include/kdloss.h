@@ -112,6 +112,10 @@ int kd_plan_query(int dtype, int64_t n, int64_t d, int64_t V, int32_t K, int64_t
  *            log-sum-exp (undefined on masked rows and padding entries)
  *   workspace: device buffer of at least plan.fwd_workspace_bytes for the same
  *            (dtype, n, d, V, K, chunk); its contents need not be initialised.
+ *            With chunk <= 0 the call itself picks the chunk: the planner's
+ *            rule with this buffer's size as the budget, fitting the forward
+ *            workspace only, so plan.fwd_workspace_bytes of an automatic plan
+ *            always suffices (KD_E_WORKSPACE if not even chunk 256 fits).
  * The result does not depend on the chunk size (bitwise, for loss and lse).
  */
 int kd_fused_chunked_kl_fwd(int dtype, const void* H, const void* W, const int32_t* topk_idx,
@@ -130,7 +134,8 @@ int kd_fused_chunked_kl_fwd(int dtype, const void* H, const void* W, const int32
  *             the caller's values; accumulate_dw == 0: OVERWRITTEN (every
  *             element written, prior contents never read, so it may be
  *             uninitialised)
- *   workspace: at least plan.bwd_workspace_bytes.
+ *   workspace: at least plan.bwd_workspace_bytes; with chunk <= 0 the chunk is
+ *             picked as in the forward call, fitting the backward workspace.
  * No gradient is produced for the teacher inputs.
  */
 int kd_fused_chunked_kl_bwd(int dtype, const void* H, const void* W, const int32_t* topk_idx,

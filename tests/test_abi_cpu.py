@@ -157,3 +157,25 @@ def test_topk_null_pointers_and_small_workspace_rejected_without_device_work():
     assert rc == -1 and b"non-null" in lib.kd_last_error_message()
     rc = lib.kd_teacher_topk(0, fake, fake, 256, 256, 4096, 16, 64, 0, fake, 16, fake, fake, None)
     assert rc == -2 and b"workspace" in lib.kd_last_error_message()
+
+
+@pytest.mark.parametrize("n,d,V,K", [(32768, 2880, 201088, 100), (4096, 3072, 128256, 100), (200, 256, 4096, 16)])
+def test_auto_chunk_calls_plan_against_their_own_workspace(n, d, V, K):
+    """chunk <= 0 with a buffer of the planner's per-call size: the forward
+    needs only plan.fwd_workspace_bytes and the backward plan.bwd_workspace_bytes.
+    A null loss / lse pointer is the next check after planning, so reaching
+    it (KD_E_INVAL, "non-null") shows the plan fitted; no device work is done."""
+    lib = kd.lib()
+    p = kd.kd_plan_query(kd.KD_BF16, n, d, V, K, 0, 200 * GiB)
+    fake = ctypes.c_void_p(4096)
+    rc = lib.kd_fused_chunked_kl_fwd(0, fake, fake, fake, fake, None, n, d, V, K, 0, 1.0, fake,
+                                     p["fwd_workspace_bytes"], None, fake, None, None, None)
+    assert rc == -1 and b"non-null" in lib.kd_last_error_message(), lib.kd_last_error_message()
+    rc = lib.kd_fused_chunked_kl_bwd(0, fake, fake, fake, fake, None, n, d, V, K, 0, 1.0, None, fake,
+                                     fake, fake, 0, fake, p["bwd_workspace_bytes"], None)
+    assert rc == -1 and b"non-null" in lib.kd_last_error_message(), lib.kd_last_error_message()
+    # one byte less than the smallest plan of that call is still reported as a workspace shortfall
+    small = kd.kd_plan_query(kd.KD_BF16, n, d, V, K, min(256, n), 200 * GiB)
+    rc = lib.kd_fused_chunked_kl_fwd(0, fake, fake, fake, fake, None, n, d, V, K, 0, 1.0, fake,
+                                     small["fwd_workspace_bytes"] - 1, None, fake, None, None, None)
+    assert rc == -2 and b"bytes" in lib.kd_last_error_message()

@@ -71,3 +71,15 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_cpu_baseline_runs_on_the_granted_host_threads(monkeypatch):
+    import numpy as np
+    cpus = len(os.sched_getaffinity(0))
+    monkeypatch.setenv("OMP_NUM_THREADS", "2")
+    assert bench.host_cpus() == (cpus, min(cpus, 2))
+    _, _, used, seen = bench.timed_oracle(lambda: np.ones((64, 64)) @ np.ones((64, 64)))
+    assert used == min(cpus, 2) and seen == cpus
+    monkeypatch.delenv("OMP_NUM_THREADS")
+    _, _, used, _ = bench.timed_oracle(lambda: None)
+    assert used == cpus
