@@ -30,7 +30,9 @@ struct Ctrl {
 enum class DType { BF16 = 0, F32 = 1 };
 
 // One unmasked teacher entry (row, k), bucketed by (vocabulary tile, 64-row
-// block): its row, k, vocabulary id and renormalised probability p_{row,k}.
+// block): its row, k, vocabulary id and the probability its scatter
+// subtracts: p_{row,k}, or for an id the row repeats, the sum of the p of all
+// its occurrences at the first one (in k order) and 0 at the others.
 struct alignas(16) Hit {
   int row;
   int k;

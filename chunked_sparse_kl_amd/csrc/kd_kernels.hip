@@ -142,19 +142,50 @@ __global__ __launch_bounds__(256) void teacher_bucket_kernel(
   }
   __syncthreads();
 
-  // Placement: p is re-read from memory this workgroup wrote before the barrier.
+  // Placement: p is re-read from memory this workgroup wrote before the
+  // barrier.  A hit's p is used only by the backward's scatter, which
+  // subtracts it from the accumulator of (row, id).  A row that repeats an id
+  // has several hits on one accumulator, and the order of their subtractions
+  // (bucket order, set by the LDS cursors) would decide the rounding.  So the
+  // first occurrence of an id in a row carries the sum of the p of all its
+  // occurrences, added in k order, and the later ones carry 0: hits of
+  // distinct (row, id) touch distinct accumulators, so G does not depend on
+  // the order within a bucket.  (The forward's gather reads every hit's own
+  // (row, k) and is order-free.)
   for (int row = row_lo + wave; row < row_hi; row += 4) {
     if (mask != nullptr && mask[row] == 0) continue;
     const long long base = (long long)row * K;
-    for (int k = lane; k < K; k += 64) {
-      const int v = idx[base + k];
-      if (v >= 0 && v < V) {
+    for (int k0 = 0; k0 < K; k0 += 64) {
+      const int k = k0 + lane;
+      const int v = k < K ? idx[base + k] : -1;
+      const bool valid = v >= 0 && v < V;
+      // first occurrence and number of occurrences of v in the row (a
+      // wave-uniform loop: every lane compares with the same entry kp)
+      int first = k, same = 0;
+      for (int kp = 0; kp < K; ++kp) {
+        const int w = idx[base + kp];
+        if (w == v) {
+          ++same;
+          first = min(first, kp);
+        }
+      }
+      const bool dup = valid && same > 1;
+      float ph = valid ? p[base + k] : 0.f;
+      if (__any(dup)) {
+        float sum = 0.f;
+        for (int kp = 0; kp < K; ++kp) {
+          const float pk = p[base + kp];
+          if (idx[base + kp] == v) sum += pk;
+        }
+        if (dup) ph = first == k ? sum : 0.f;
+      }
+      if (valid) {
         const int pos = atomicAdd(&cnt[v / TILE_V], 1);
         Hit h;
         h.row = row;
         h.k = k;
         h.v = v;
-        h.p = p[base + k];
+        h.p = ph;
         hits[hit_base + pos] = h;
       }
     }

@@ -187,6 +187,28 @@ def test_deterministic_repeat():
         assert np.array_equal(a[k], b[k]), k
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_deterministic_repeat_with_duplicate_ids(dtype):
+    # K = 100 (two 64-lane chunks per row): rows repeat ids within and across
+    # the chunks, two and three times, several rows share a vocabulary tile
+    inp = synth.make_custom(640, 192, 1500, 100, dtype, "random5", "uniform", seed=27)
+    idx = inp["idx"].numpy()
+    rng = np.random.default_rng(27)
+    for t in range(0, 640, 3):
+        src = rng.choice(100, size=12, replace=False)
+        dst = rng.choice(100, size=12, replace=False)
+        idx[t, dst] = idx[t, src]
+    idx[1, 70:] = idx[1, :30]                      # across the 64-entry boundary
+    idx[2, [0, 64, 99]] = idx[2, 5]                # three occurrences
+    inp["idx"] = torch.from_numpy(idx)
+    runs = [run_gpu(inp, chunk=128, grad=0.6) for _ in range(3)]
+    for r in runs[1:]:
+        assert r["loss"] == runs[0]["loss"]
+        for k in ("lse", "row_kl", "g", "dH", "dW"):
+            assert np.array_equal(r[k], runs[0][k]), k
+    check_full(inp, runs[0], dtype, grad=0.6)
+
+
 @pytest.mark.parametrize("chunk", [520, 192, 128])
 def test_dw_overwrite_mode(chunk):
     """accumulate=False never reads dW (NaN-filled here) and matches a fresh
