@@ -20,7 +20,8 @@ __all__ = [
     "KD_BF16", "KD_F32", "KdError", "kd_plan_query", "kd_fused_chunked_kl_fwd",
     "kd_fused_chunked_kl_bwd", "kd_set_validate", "kd_profile_enable", "kd_profile_reset",
     "kd_profile_read", "fused_chunked_kl", "library_path", "EXPORTED_SYMBOLS", "lib",
-    "kd_teacher_topk_plan", "kd_teacher_topk",
+    "kd_teacher_topk_plan", "kd_teacher_topk", "kd_fused_chunked_kl_fwd_noalloc",
+    "KD_NOALLOC_SCRATCH_BYTES",
 ]
 
 KD_BF16 = 0
@@ -31,8 +32,10 @@ EXPORTED_SYMBOLS = (
     "kd_plan_query", "kd_fused_chunked_kl_fwd", "kd_fused_chunked_kl_bwd", "kd_status_string",
     "kd_last_error_message", "kd_set_validate", "kd_profile_enable", "kd_profile_reset",
     "kd_profile_read",
-    "kd_teacher_topk_plan", "kd_teacher_topk",
+    "kd_teacher_topk_plan", "kd_teacher_topk", "kd_fused_chunked_kl_fwd_noalloc",
 )
+
+KD_NOALLOC_SCRATCH_BYTES = 256 << 20
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -83,6 +86,8 @@ def _load():
     lib.kd_fused_chunked_kl_bwd.argtypes = [
         ctypes.c_int, vp, vp, vp, vp, vp, i64, i64, i64, i32, i64, f32, vp, vp, vp, vp, ctypes.c_int,
         vp, sz, vp]
+    lib.kd_fused_chunked_kl_fwd_noalloc.argtypes = [
+        ctypes.c_int, vp, vp, vp, vp, vp, i64, i64, i64, i32, i64, f32, vp, vp, vp, vp, vp]
     lib.kd_status_string.argtypes = [ctypes.c_int]
     lib.kd_status_string.restype = ctypes.c_char_p
     lib.kd_last_error_message.argtypes = []
@@ -94,7 +99,8 @@ def _load():
     lib.kd_teacher_topk_plan.argtypes = [ctypes.c_int, i64, i64, i64, i32, i64, i64, sz,
                                          ctypes.POINTER(KdTopkPlan)]
     lib.kd_teacher_topk.argtypes = [ctypes.c_int, vp, vp, i64, i64, i64, i32, i64, i64, vp, sz, vp, vp, vp]
-    for f in ("kd_plan_query", "kd_fused_chunked_kl_fwd", "kd_fused_chunked_kl_bwd",
+    for f in ("kd_plan_query", "kd_fused_chunked_kl_fwd", "kd_fused_chunked_kl_fwd_noalloc",
+              "kd_fused_chunked_kl_bwd",
               "kd_set_validate", "kd_profile_enable", "kd_profile_reset", "kd_profile_read",
               "kd_teacher_topk_plan", "kd_teacher_topk"):
         getattr(lib, f).restype = ctypes.c_int
@@ -191,6 +197,33 @@ def kd_fused_chunked_kl_fwd(H, W, topk_idx, topk_logp, mask=None, chunk: int = 0
         plan["chunk"], float(temperature), _ptr(ws), ws.numel() * ws.element_size(), _ptr(loss),
         _ptr(lse), _ptr(rk), _ptr(g), _stream(H.device)))
     return {"loss": loss, "lse": lse, "row_kl": rk, "gathered": g, "plan": plan}
+
+
+def kd_fused_chunked_kl_fwd_noalloc(H, W, topk_idx, topk_logp, mask=None, chunk: int = 0,
+                                    temperature: float = 1.0, loss=None, lse=None, row_kl=None,
+                                    gathered=None):
+    """Forward call that allocates nothing on the device: the library's
+    per-GPU scratch array (KD_NOALLOC_SCRATCH_BYTES) is its workspace.  The
+    outputs may be passed in (loss [1], lse [n], row_kl [n] or None, gathered
+    [n, K] or None, fp32 device tensors); the ones left as None that are
+    required (loss, lse) are allocated here, by torch, before the call.
+    Returns a dict like kd_fused_chunked_kl_fwd's (without a plan).  Calls
+    that overlap on one GPU share the scratch and must be serialised."""
+    n, d, V, K = _check_inputs(H, W, topk_idx, topk_logp, mask)
+    dt = _dtype_code(H)
+    if loss is None:
+        loss = torch.empty(1, dtype=torch.float32, device=H.device)
+    if lse is None:
+        lse = torch.empty(n, dtype=torch.float32, device=H.device)
+    for name, t, shape in (("loss", loss, (1,)), ("lse", lse, (n,)), ("row_kl", row_kl, (n,)),
+                           ("gathered", gathered, (n, K))):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != shape
+                              or not t.is_contiguous() or t.device != H.device):
+            raise ValueError(f"{name} must be a contiguous float32 {list(shape)} tensor on H's device")
+    _check(lib().kd_fused_chunked_kl_fwd_noalloc(
+        dt, _ptr(H), _ptr(W), _ptr(topk_idx), _ptr(topk_logp), _ptr(mask), n, d, V, K, chunk,
+        float(temperature), _ptr(loss), _ptr(lse), _ptr(row_kl), _ptr(gathered), _stream(H.device)))
+    return {"loss": loss, "lse": lse, "row_kl": row_kl, "gathered": gathered}
 
 
 def kd_fused_chunked_kl_bwd(H, W, topk_idx, topk_logp, mask, lse, grad_loss=None, chunk: int = 0,

@@ -11,6 +11,7 @@
 #include <cstdlib>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -52,6 +53,9 @@ struct Record {
   double flops, bytes;
 };
 bool g_profile = false;
+// Set while a call that creates no runtime objects runs (the no-allocation
+// forward): its launches are not timed, since timing creates events.
+thread_local bool g_no_events = false;
 std::vector<Record> g_records;
 struct Agg {
   std::string name;
@@ -64,7 +68,8 @@ struct Timed {
   Record r{};
   hipStream_t s;
   bool on;
-  Timed(hipStream_t st, const char* name, double flops, double bytes) : s(st), on(g_profile) {
+  Timed(hipStream_t st, const char* name, double flops, double bytes)
+      : s(st), on(g_profile && !g_no_events) {
     if (!on) return;
     r.name = name;
     r.flops = flops;
@@ -433,6 +438,88 @@ int topk_plan(int dtype, int64_t n, int64_t d, int64_t V, int64_t K, int64_t chu
               L.end, budget);
 }
 
+// The forward's launch sequence on a planned layout and a workspace of at
+// least L.fwd_end bytes (arguments already checked).
+int run_forward(const Layout& L, const void* H, const void* W, const int32_t* topk_idx,
+                const float* topk_logp, const uint8_t* mask, float temperature, void* workspace,
+                float* loss, float* lse, float* row_kl, float* gathered, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  int rc = prepare_teacher(L, topk_idx, topk_logp, mask, temperature, ws, s);
+  if (rc != KD_OK) return rc;
+
+  const size_t es = kd::elem_size(L.dt);
+  float* g = gathered != nullptr ? gathered : reinterpret_cast<float*>(ws + L.g);
+  float* rk = row_kl != nullptr ? row_kl : reinterpret_cast<float*>(ws + L.rowkl);
+  auto* part = reinterpret_cast<float2*>(ws + L.part);
+  for (int64_t c0 = 0; c0 < L.n; c0 += L.chunk) {
+    const int rows = (int)std::min<int64_t>(L.chunk, L.n - c0);
+    kd::FwdEpilogue ep{};
+    ep.part = part;
+    ep.ld_part = (int)L.chunk;
+    ep.n_vt = (int)L.n_vt;
+    ep.c0 = (int)c0;
+    ep.rows = rows;
+    ep.V = (int)L.V;
+    ep.K = (int)L.K;
+    ep.hit_ld = (int)L.n_vt + 1;
+    ep.hit_off = reinterpret_cast<const int*>(ws + L.hit_off);
+    ep.hits = reinterpret_cast<const kd::Hit*>(ws + L.hits);
+    ep.g = g;
+    ep.inv_tau = 1.0f / temperature;
+    const char* Hc = static_cast<const char*>(H) + c0 * L.d * es;
+    const double fl = 2.0 * rows * L.d * L.V;
+    const double by = double(L.V) * L.d * es + double(rows) * L.d * es + double(rows) * L.n_vt * 8;
+    KD_LAUNCH("fwd_gemm", fl, by, kd::launch_fwd_gemm(L.dt, W, (int)L.V, Hc, rows, (int)L.d, ep, s));
+    KD_LAUNCH("lse_kl", 0, double(rows) * (L.n_vt * 8 + L.K * 8 + 16),
+              kd::launch_lse_kl(part, (int)L.chunk, (int)L.n_vt, (int)c0, rows,
+                                reinterpret_cast<const float*>(ws + L.p), g,
+                                reinterpret_cast<const float*>(ws + L.S),
+                                reinterpret_cast<const float*>(ws + L.E), mask, (int)L.K,
+                                temperature, lse, rk, s));
+  }
+  KD_LAUNCH("loss", 0, L.n * 4.0,
+            kd::launch_loss(rk, (int)L.n, reinterpret_cast<const kd::Ctrl*>(ws + L.ctrl), loss, s));
+  return ok();
+}
+
+// ------------------------------------------------------------------ no-allocation forward
+// The workspace of kd_fused_chunked_kl_fwd_noalloc: a file-scope device array,
+// one per GPU the library runs on, held until the process ends.  Host code
+// never uses the array's name as an address (on the host it names a stand-in,
+// not device memory): the device address comes from hipGetSymbolAddress, once
+// per device, with that device current.
+static __device__ __align__(256) unsigned char scratch[KD_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array.
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(KD_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(KD_E_INVAL, "device %d is beyond the %d devices the scratch table holds", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(KD_E_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  e != hipSuccess ? hipGetErrorString(e) : "null address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return KD_OK;
+}
+
+struct NoEvents {
+  NoEvents() { g_no_events = true; }
+  ~NoEvents() { g_no_events = false; }
+};
+
 }  // namespace
 
 extern "C" {
@@ -512,44 +599,35 @@ int kd_fused_chunked_kl_fwd(int dtype, const void* H, const void* W, const int32
   if (rc != KD_OK) return rc;
   rc = check_common(H, W, topk_idx, topk_logp, workspace, workspace_bytes, L.fwd_end);
   if (rc != KD_OK) return rc;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  rc = prepare_teacher(L, topk_idx, topk_logp, mask, temperature, ws, s);
-  if (rc != KD_OK) return rc;
+  return run_forward(L, H, W, topk_idx, topk_logp, mask, temperature, workspace, loss, lse, row_kl,
+                     gathered, stream);
+}
 
-  const size_t es = kd::elem_size(L.dt);
-  float* g = gathered != nullptr ? gathered : reinterpret_cast<float*>(ws + L.g);
-  float* rk = row_kl != nullptr ? row_kl : reinterpret_cast<float*>(ws + L.rowkl);
-  auto* part = reinterpret_cast<float2*>(ws + L.part);
-  for (int64_t c0 = 0; c0 < L.n; c0 += L.chunk) {
-    const int rows = (int)std::min<int64_t>(L.chunk, L.n - c0);
-    kd::FwdEpilogue ep{};
-    ep.part = part;
-    ep.ld_part = (int)L.chunk;
-    ep.n_vt = (int)L.n_vt;
-    ep.c0 = (int)c0;
-    ep.rows = rows;
-    ep.V = (int)L.V;
-    ep.K = (int)L.K;
-    ep.hit_ld = (int)L.n_vt + 1;
-    ep.hit_off = reinterpret_cast<const int*>(ws + L.hit_off);
-    ep.hits = reinterpret_cast<const kd::Hit*>(ws + L.hits);
-    ep.g = g;
-    ep.inv_tau = 1.0f / temperature;
-    const char* Hc = static_cast<const char*>(H) + c0 * L.d * es;
-    const double fl = 2.0 * rows * L.d * L.V;
-    const double by = double(L.V) * L.d * es + double(rows) * L.d * es + double(rows) * L.n_vt * 8;
-    KD_LAUNCH("fwd_gemm", fl, by, kd::launch_fwd_gemm(L.dt, W, (int)L.V, Hc, rows, (int)L.d, ep, s));
-    KD_LAUNCH("lse_kl", 0, double(rows) * (L.n_vt * 8 + L.K * 8 + 16),
-              kd::launch_lse_kl(part, (int)L.chunk, (int)L.n_vt, (int)c0, rows,
-                                reinterpret_cast<const float*>(ws + L.p), g,
-                                reinterpret_cast<const float*>(ws + L.S),
-                                reinterpret_cast<const float*>(ws + L.E), mask, (int)L.K,
-                                temperature, lse, rk, s));
-  }
-  KD_LAUNCH("loss", 0, L.n * 4.0,
-            kd::launch_loss(rk, (int)L.n, reinterpret_cast<const kd::Ctrl*>(ws + L.ctrl), loss, s));
-  return ok();
+int kd_fused_chunked_kl_fwd_noalloc(int dtype, const void* H, const void* W, const int32_t* topk_idx,
+                                    const float* topk_logp, const uint8_t* mask, int64_t n, int64_t d,
+                                    int64_t V, int32_t K, int64_t chunk, float temperature, float* loss,
+                                    float* lse, float* row_kl, float* gathered, void* stream) {
+  Layout L;
+  int rc = plan(dtype, n, d, V, K, chunk, KD_NOALLOC_SCRATCH_BYTES, &L, Fit::kFwd);
+  if (rc == KD_E_WORKSPACE)
+    return fail(KD_E_WORKSPACE, "too large for the no-allocation forward's scratch of %llu bytes (%s)",
+                (unsigned long long)KD_NOALLOC_SCRATCH_BYTES, g_last_error.c_str());
+  if (rc != KD_OK) return rc;
+  if (L.fwd_end > KD_NOALLOC_SCRATCH_BYTES)
+    return fail(KD_E_WORKSPACE,
+                "chunk %lld needs %zu bytes of workspace; the no-allocation forward's scratch holds %llu",
+                (long long)L.chunk, L.fwd_end, (unsigned long long)KD_NOALLOC_SCRATCH_BYTES);
+  if (loss == nullptr || lse == nullptr) return fail(KD_E_INVAL, "loss and lse must be non-null");
+  rc = check_temperature(temperature);
+  if (rc != KD_OK) return rc;
+  void* ws = nullptr;
+  rc = scratch_of_current_device(&ws);
+  if (rc != KD_OK) return rc;
+  rc = check_common(H, W, topk_idx, topk_logp, ws, KD_NOALLOC_SCRATCH_BYTES, L.fwd_end);
+  if (rc != KD_OK) return rc;
+  NoEvents no_events;
+  return run_forward(L, H, W, topk_idx, topk_logp, mask, temperature, ws, loss, lse, row_kl, gathered,
+                     stream);
 }
 
 int kd_fused_chunked_kl_bwd(int dtype, const void* H, const void* W, const int32_t* topk_idx,

@@ -125,6 +125,29 @@ int kd_fused_chunked_kl_fwd(int dtype, const void* H, const void* W, const int32
                             float* gathered, void* stream);
 
 /*
+ * Forward without allocation, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving or evaluation loops, harnesses
+ * that forbid hipMalloc).  Same arguments, results and kernels as
+ * kd_fused_chunked_kl_fwd, without the workspace: the call uses a scratch
+ * array of KD_NOALLOC_SCRATCH_BYTES that the library holds in every GPU it
+ * runs on until the process ends, and calls no hipMalloc, hipFree or other
+ * allocating routine, nor creates events (kernel timing skips these calls).
+ * With chunk <= 0 the largest automatic chunk whose forward workspace fits
+ * the scratch is used; a problem whose forward workspace does not fit even at
+ * chunk 256 (or at the chunk given) returns KD_E_WORKSPACE before any device
+ * work (the 32K-token, 201088-vocabulary, K = 100 forward needs 126 MiB).
+ * Every call on one GPU shares that GPU's scratch and leaves its contents
+ * behind: calls that overlap on one GPU (several streams or host threads)
+ * race and must be serialised by the caller.  The current device must be the
+ * stream's.
+ */
+#define KD_NOALLOC_SCRATCH_BYTES (256ull << 20)
+int kd_fused_chunked_kl_fwd_noalloc(int dtype, const void* H, const void* W, const int32_t* topk_idx,
+                                    const float* topk_logp, const uint8_t* mask, int64_t n, int64_t d,
+                                    int64_t V, int32_t K, int64_t chunk, float temperature, float* loss,
+                                    float* lse, float* row_kl, float* gathered, void* stream);
+
+/*
  * Backward: recomputes each chunk's logits from H and W, forms G in registers
  * (rounded to the input dtype), then dH = G W and dW (+)= G^T H.
  *   lse       [n] fp32 device: exactly what kd_fused_chunked_kl_fwd wrote
