@@ -56,11 +56,90 @@ __device__ inline int block256_exclusive_scan(int v, int* sh, int* total) {
   return base + incl - v;
 }
 
+// Per-wavefront table that finds the ids a row repeats: open addressing over
+// kDupSlots slots of (id, smallest k, largest k); rows with K <= kDupSlots / 2
+// use it (load factor <= 1/2), longer rows compare every pair of entries.
+constexpr int kDupSlots = 256;
+
+// For one row (ids[0..K), p[0..K) as stored, p_of(k) recomputes p bitwise):
+// where an id occurs more than once, p at its first occurrence becomes the
+// sum of its occurrences' p in k order and p at the others becomes 0.
+// Ids < 0 or >= V are left alone.  Called by a whole wavefront.
+template <class PK>
+__device__ inline void resolve_repeated_ids(const int* ids, int K, int V, float* p, int* tab, PK&& p_of) {
+  const int lane = threadIdx.x & 63;
+  constexpr int kMaxChunks = kDupSlots / 2 / 64;
+  int first[kMaxChunks], last[kMaxChunks];
+  if (K <= kDupSlots / 2) {
+    int* const t_id = tab;
+    int* const t_min = tab + kDupSlots;
+    int* const t_max = tab + 2 * kDupSlots;
+    for (int i = lane; i < kDupSlots; i += 64) {
+      t_id[i] = -1;
+      t_min[i] = 0x7fffffff;
+      t_max[i] = -1;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    int slot[kMaxChunks];
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {
+      const int k = 64 * c + lane;
+      slot[c] = -1;
+      const int v = k < K ? ids[k] : -1;
+      if (v >= 0 && v < V) {
+        int h = (int)(((unsigned)v * 2654435761u) >> 24);  // Fibonacci hash to 8 bits
+        for (;;) {
+          const int old = atomicCAS(&t_id[h], -1, v);
+          if (old == -1 || old == v) break;
+          h = (h + 1) & (kDupSlots - 1);
+        }
+        atomicMin(&t_min[h], k);
+        atomicMax(&t_max[h], k);
+        slot[c] = h;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {
+      first[c] = slot[c] >= 0 ? t_min[slot[c]] : 0;
+      last[c] = slot[c] >= 0 ? t_max[slot[c]] : 0;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // the table is cleared for the next row after this
+    bool any_dup = false;
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) any_dup |= first[c] != last[c];
+    if (!__any(any_dup)) return;  // the common case: no repeated id in the row
+  }
+  // first / last occurrence by comparing with every entry (long rows, or the
+  // rows of the table path that repeat an id), then the sums in k order
+  for (int k0 = 0; k0 < K; k0 += 64) {
+    const int k = k0 + lane;
+    const int v = k < K ? ids[k] : -1;
+    int f = k, n_same = 0;
+    float sum = 0.f;
+    for (int kq = 0; kq < K; kq += 64) {
+      const int wv = kq + lane < K ? ids[kq + lane] : -1;
+      const float pv = kq + lane < K ? p_of(kq + lane) : 0.f;
+      const int here = min(64, K - kq);
+      for (int u = 0; u < here; ++u) {
+        const float pu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pv), u));
+        if (__builtin_amdgcn_readlane(wv, u) == v) {
+          ++n_same;
+          f = min(f, kq + u);
+          sum += pu;
+        }
+      }
+    }
+    if (v >= 0 && v < V && n_same > 1) p[k] = f == k ? sum : 0.f;
+  }
+}
+
 // One workgroup (4 wavefronts) per 64-row block.  Each wavefront takes one row
 // at a time: renormalises the teacher's K log-values (the offline top-K cache
-// of the blog's "Two systems changes"), stores p = exp(l), S = sum p and
-// E = sum p*l (0*log 0 := 0), and counts the row's ids per vocabulary tile in
-// LDS.  The counts are then scanned into this block's bucket offsets and every
+// of the blog's "Two systems changes"), computes p = exp(l), S = sum p and
+// E = sum p*l (0*log 0 := 0), stores p (for an id the row repeats: the sum
+// of its occurrences' p at the first one, 0 at the others), and counts the
+// row's ids per vocabulary tile in LDS.  The counts are then scanned into this block's bucket offsets and every
 // entry is placed in its bucket with LDS cursors.  Masked rows are skipped
 // entirely; ids >= V set the range flag and are dropped; ids < 0 are padding
 // (probability 0, outside the renormalisation).  The log-values are divided
@@ -69,12 +148,13 @@ __global__ __launch_bounds__(256) void teacher_bucket_kernel(
     const float* __restrict__ logp, const int* __restrict__ idx, const uint8_t* __restrict__ mask,
     int n, int K, int V, int n_vt, float inv_tau, float* __restrict__ p, float* __restrict__ S,
     float* __restrict__ E, int* __restrict__ hit_off, Hit* __restrict__ hits, Ctrl* ctrl) {
-  extern __shared__ int cnt[];  // n_vt + 1 counters, then cursors
+  extern __shared__ int cnt[];  // n_vt + 1 counters (then cursors), then the repeated-id tables
   __shared__ int sh[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rb = blockIdx.x;
   const int row_lo = rb * ROW_BLOCK, row_hi = min(row_lo + ROW_BLOCK, n);
   const int n_ct = n_vt + 1;
+  int* const dup_tab = cnt + n_ct;  // 4 wavefronts x 3 x kDupSlots
   for (int j = tid; j < n_ct; j += 256) cnt[j] = 0;
   __syncthreads();
 
@@ -119,6 +199,18 @@ __global__ __launch_bounds__(256) void teacher_bucket_kernel(
       S[row] = sp;
       E[row] = e;
     }
+    // Repeated ids.  The backward's scatter subtracts each entry's p from the
+    // accumulator of (row, id), and entries reach it in the order of their
+    // teacher-hit bucket, which the LDS cursors below make arbitrary; a
+    // repeated id would put several subtractions on one accumulator in that
+    // order.  So the first occurrence of an id keeps the sum of the p of all
+    // its occurrences (added in k order) and the later ones keep 0: entries
+    // of distinct (row, id) touch distinct accumulators and the result no
+    // longer depends on the bucket order.  The forward's sum of p * g is the
+    // same sum (repeated ids share one logit g); S and E above use every p.
+    resolve_repeated_ids(idx + base, K, V, p + base, dup_tab + wave * 3 * kDupSlots, [&](int k) {
+      return expf(a_of(k) - lam);  // bitwise the p stored above
+    });
   }
   if (lane == 0 && live_rows > 0) atomicAdd(&ctrl->n_valid, live_rows);
   if (__any(bad) && lane == 0) ctrl->range_error = 1;
@@ -142,50 +234,19 @@ __global__ __launch_bounds__(256) void teacher_bucket_kernel(
   }
   __syncthreads();
 
-  // Placement: p is re-read from memory this workgroup wrote before the
-  // barrier.  A hit's p is used only by the backward's scatter, which
-  // subtracts it from the accumulator of (row, id).  A row that repeats an id
-  // has several hits on one accumulator, and the order of their subtractions
-  // (bucket order, set by the LDS cursors) would decide the rounding.  So the
-  // first occurrence of an id in a row carries the sum of the p of all its
-  // occurrences, added in k order, and the later ones carry 0: hits of
-  // distinct (row, id) touch distinct accumulators, so G does not depend on
-  // the order within a bucket.  (The forward's gather reads every hit's own
-  // (row, k) and is order-free.)
+  // Placement: p is re-read from memory this workgroup wrote before the barrier.
   for (int row = row_lo + wave; row < row_hi; row += 4) {
     if (mask != nullptr && mask[row] == 0) continue;
     const long long base = (long long)row * K;
-    for (int k0 = 0; k0 < K; k0 += 64) {
-      const int k = k0 + lane;
-      const int v = k < K ? idx[base + k] : -1;
-      const bool valid = v >= 0 && v < V;
-      // first occurrence and number of occurrences of v in the row (a
-      // wave-uniform loop: every lane compares with the same entry kp)
-      int first = k, same = 0;
-      for (int kp = 0; kp < K; ++kp) {
-        const int w = idx[base + kp];
-        if (w == v) {
-          ++same;
-          first = min(first, kp);
-        }
-      }
-      const bool dup = valid && same > 1;
-      float ph = valid ? p[base + k] : 0.f;
-      if (__any(dup)) {
-        float sum = 0.f;
-        for (int kp = 0; kp < K; ++kp) {
-          const float pk = p[base + kp];
-          if (idx[base + kp] == v) sum += pk;
-        }
-        if (dup) ph = first == k ? sum : 0.f;
-      }
-      if (valid) {
+    for (int k = lane; k < K; k += 64) {
+      const int v = idx[base + k];
+      if (v >= 0 && v < V) {
         const int pos = atomicAdd(&cnt[v / TILE_V], 1);
         Hit h;
         h.row = row;
         h.k = k;
         h.v = v;
-        h.p = ph;
+        h.p = p[base + k];
         hits[hit_base + pos] = h;
       }
     }
@@ -374,7 +435,7 @@ void launch_teacher_bucket(const float* logp, const int* idx, const uint8_t* mas
                            Hit* hits, Ctrl* ctrl, hipStream_t s) {
   const int n_vt = (V + TILE_V - 1) / TILE_V;
   const int n_rb = (n + ROW_BLOCK - 1) / ROW_BLOCK;
-  const size_t lds = size_t(n_vt + 1) * sizeof(int);
+  const size_t lds = (size_t(n_vt + 1) + 4 * 3 * kDupSlots) * sizeof(int);
   teacher_bucket_kernel<<<n_rb, 256, lds, s>>>(logp, idx, mask, n, K, V, n_vt, inv_tau, p, S, E,
                                                hit_off, hits, ctrl);
 }

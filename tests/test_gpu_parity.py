@@ -200,7 +200,12 @@ def test_deterministic_repeat_with_duplicate_ids(dtype):
         idx[t, dst] = idx[t, src]
     idx[1, 70:] = idx[1, :30]                      # across the 64-entry boundary
     idx[2, [0, 64, 99]] = idx[2, 5]                # three occurrences
+    idx[4, :] = idx[4, 7]                          # one id, 100 times
+    idx[5, :] = np.tile(idx[5, :5], 20)            # five ids, 20 times each
+    idx[6, ::2] = -1                               # padding between repeats
+    idx[6, 1::4] = idx[6, 3]
     inp["idx"] = torch.from_numpy(idx)
+    inp["mask"][[4, 5, 6]] = 1
     runs = [run_gpu(inp, chunk=128, grad=0.6) for _ in range(3)]
     for r in runs[1:]:
         assert r["loss"] == runs[0]["loss"]
