@@ -195,48 +195,97 @@ def topk_builder_main(args) -> int:
 
 
 def memory_sweep_main(args) -> int:
-    """Peak device memory of one fwd+bwd against T at d=3072, V=128256, K=100
-    (the long-context workload's shapes; values are random device tensors:
-    memory does not depend on them), with the planner choosing the chunk.
-    Fits peak = a + b*T by least squares over the sizes at the planner's
-    largest chunk and prints the points, a, b and the largest residual."""
+    """Peak device memory and time of one fwd+bwd against T at d=3072,
+    V=128256, K=100 (the long-context workload's shapes; values are random
+    device tensors: memory and time do not depend on them), with the planner
+    choosing the chunk, for the fused path and, with --variants, the two
+    comparison variants (dense KL, forward-chunked KL).  A variant that fails
+    to allocate at some T is recorded there and not run at larger T.  Fits
+    the fused path's peak = a + b*T by least squares over the sizes at the
+    planner's largest chunk."""
     import torch
     import chunked_sparse_kl_amd as kd
 
     dev = torch.device("cuda", 0)
     d, V, K = 3072, 128256, 100
-    Ts = [4096, 8192, 16384, 32768, 65536, 131072, 262144]
+    Ts = [int(t) for t in args.sweep_tokens.split(",")]
+    variants = args.variants.split(",")
+    calls = {"fused": (kd.kd_fused_chunked_kl_fwd, kd.kd_fused_chunked_kl_bwd),
+             "forward_chunked": (kd.kd_forward_chunked_kl_fwd, kd.kd_forward_chunked_kl_bwd),
+             "dense": (kd.kd_dense_kl_fwd, kd.kd_dense_kl_bwd)}
     g = torch.Generator(device=dev).manual_seed(5)
     W = (torch.randn(V, d, device=dev, generator=g) * d ** -0.5).to(torch.bfloat16)
-    pts = []
+    total = torch.cuda.get_device_properties(dev).total_memory
+    pts = {v: [] for v in variants}
+    failed_at = {v: None for v in variants}
+
+    def one_step(var, H, idx, logp, dW):
+        fwd, bwd = calls[var]
+        if var == "fused":
+            fw = fwd(H, W, idx, logp, None, row_kl=False)
+            bwd(H, W, idx, logp, None, fw["lse"], plan=fw["plan"], dW=dW, accumulate=False)
+        else:
+            fw = fwd(H, W, idx, logp, None, row_kl=False)
+            bwd(H, W, idx, logp, None, fw["lse"], fw["grid"], plan=fw["plan"], dW=dW, accumulate=False)
+        return fw
+
     for T in Ts:
         H = torch.randn(T, d, device=dev, generator=g).to(torch.bfloat16)
         idx = torch.randint(0, V, (T, K), device=dev, dtype=torch.int32, generator=g)
         logp = torch.randn(T, K, device=dev, generator=g)
-        torch.cuda.synchronize()
-        torch.cuda.reset_peak_memory_stats(dev)
-        fw = kd.kd_fused_chunked_kl_fwd(H, W, idx, logp, None, row_kl=False)
-        dH, dW = kd.kd_fused_chunked_kl_bwd(H, W, idx, logp, None, fw["lse"], plan=fw["plan"])
-        torch.cuda.synchronize()
-        peak = torch.cuda.max_memory_allocated(dev)
-        pts.append({"T": T, "peak_gib": round(peak / 2**30, 4), "chunk": fw["plan"]["chunk"],
-                    "loss_finite": bool(torch.isfinite(fw["loss"]).item())})
-        log(f"T={T}: peak {peak / 2**30:.3f} GiB, chunk {fw['plan']['chunk']}")
-        del H, idx, logp, fw, dH, dW
+        for var in variants:
+            if failed_at[var] is not None:
+                continue
+            dW = torch.empty((V, d), dtype=torch.float32, device=dev)
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+            torch.cuda.reset_peak_memory_stats(dev)
+            try:
+                fw = one_step(var, H, idx, logp, dW)
+                torch.cuda.synchronize()
+                peak = torch.cuda.max_memory_allocated(dev)
+                loss_ok = bool(torch.isfinite(fw["loss"]).item())
+                chunk = fw["plan"]["chunk"]
+                del fw
+                t0 = time.perf_counter()
+                for _ in range(args.sweep_steps):
+                    fw = one_step(var, H, idx, logp, dW)
+                    del fw
+                torch.cuda.synchronize()
+                ms = (time.perf_counter() - t0) / args.sweep_steps * 1e3
+                pts[var].append({"T": T, "peak_gib": round(peak / 2**30, 4), "ms_per_step": round(ms, 2),
+                                 "chunk": chunk, "loss_finite": loss_ok})
+                log(f"{var:16s} T={T}: peak {peak / 2**30:.3f} GiB, {ms:.1f} ms/step, chunk {chunk}")
+            except torch.cuda.OutOfMemoryError as e:
+                failed_at[var] = T
+                pts[var].append({"T": T, "out_of_memory": True,
+                                 "message": str(e).splitlines()[0][:200]})
+                log(f"{var:16s} T={T}: out of device memory")
+            finally:
+                fw = None
+                del dW
+                torch.cuda.synchronize()
+                torch.cuda.empty_cache()
+        del H, idx, logp
         torch.cuda.empty_cache()
-    # The planner's chunk grows with T up to its maximum; from there on the
-    # workspace is fixed and peak memory is a + b*T.
-    cmax = max(p["chunk"] for p in pts)
-    fit_pts = [p for p in pts if p["chunk"] == cmax]
-    t = np.array([p["T"] for p in fit_pts], dtype=np.float64)
-    y = np.array([p["peak_gib"] for p in fit_pts]) * 2**30
-    b, a = np.polyfit(t, y, 1)
-    resid = y - (a + b * t)
-    out = {"metric": "peak device memory vs tokens (fwd+bwd)", "d": d, "V": V, "K": K, "points": pts,
-           "fit": {"over_T": [p["T"] for p in fit_pts], "chunk": cmax, "a_gib": round(a / 2**30, 4),
-                   "b_bytes_per_token": round(b, 1),
-                   "max_abs_residual_gib": round(float(np.abs(resid).max()) / 2**30, 5)},
+    out = {"metric": "peak device memory and time vs tokens (fwd+bwd)", "d": d, "V": V, "K": K,
+           "device_memory_gib": round(total / 2**30, 2), "variants": pts,
+           "first_T_out_of_memory": failed_at,
            "full_logits_fp32_gib_at_256k": round(262144 * V * 4 / 2**30, 1)}
+    fused = [p for p in pts.get("fused", []) if "peak_gib" in p]
+    if len(fused) >= 2:
+        # the planner's chunk grows with T up to its maximum; from there on the
+        # workspace is fixed and peak memory is a + b*T
+        cmax = max(p["chunk"] for p in fused)
+        fit_pts = [p for p in fused if p["chunk"] == cmax]
+        if len(fit_pts) >= 2:
+            t = np.array([p["T"] for p in fit_pts], dtype=np.float64)
+            y = np.array([p["peak_gib"] for p in fit_pts]) * 2**30
+            b, a = np.polyfit(t, y, 1)
+            resid = y - (a + b * t)
+            out["fused_fit"] = {"over_T": [p["T"] for p in fit_pts], "chunk": cmax,
+                                "a_gib": round(a / 2**30, 4), "b_bytes_per_token": round(b, 1),
+                                "max_abs_residual_gib": round(float(np.abs(resid).max()) / 2**30, 5)}
     print(json.dumps(out), flush=True)
     return 0
 
@@ -257,7 +306,12 @@ def main() -> int:
                     help="time the teacher top-K cache builder instead of the loss step")
     ap.add_argument("--cpu-rows-topk", type=int, default=512, help="rows of the builder's oracle sample")
     ap.add_argument("--memory-sweep", action="store_true",
-                    help="peak device memory of fwd+bwd against T (4K .. 256K tokens) and its linear fit")
+                    help="peak device memory and time of fwd+bwd against T (4K .. 256K tokens)")
+    ap.add_argument("--variants", default="fused",
+                    help="memory sweep: comma-separated of fused, forward_chunked, dense")
+    ap.add_argument("--sweep-tokens", default="4096,8192,16384,32768,65536,131072,262144",
+                    help="memory sweep: the token counts")
+    ap.add_argument("--sweep-steps", type=int, default=2, help="memory sweep: timed steps per point")
     args = ap.parse_args()
     if args.copy_calibration:
         import torch

@@ -21,7 +21,9 @@ __all__ = [
     "kd_fused_chunked_kl_bwd", "kd_set_validate", "kd_profile_enable", "kd_profile_reset",
     "kd_profile_read", "fused_chunked_kl", "library_path", "EXPORTED_SYMBOLS", "lib",
     "kd_teacher_topk_plan", "kd_teacher_topk", "kd_fused_chunked_kl_fwd_noalloc",
-    "KD_NOALLOC_SCRATCH_BYTES",
+    "KD_NOALLOC_SCRATCH_BYTES", "KD_VARIANT_DENSE", "KD_VARIANT_FORWARD_CHUNKED",
+    "kd_comparator_grid_bytes", "kd_dense_kl_fwd", "kd_dense_kl_bwd", "kd_forward_chunked_kl_fwd",
+    "kd_forward_chunked_kl_bwd",
 ]
 
 KD_BF16 = 0
@@ -33,7 +35,12 @@ EXPORTED_SYMBOLS = (
     "kd_last_error_message", "kd_set_validate", "kd_profile_enable", "kd_profile_reset",
     "kd_profile_read",
     "kd_teacher_topk_plan", "kd_teacher_topk", "kd_fused_chunked_kl_fwd_noalloc",
+    "kd_comparator_grid_bytes", "kd_dense_kl_fwd", "kd_dense_kl_bwd", "kd_forward_chunked_kl_fwd",
+    "kd_forward_chunked_kl_bwd",
 )
+
+KD_VARIANT_DENSE = 1
+KD_VARIANT_FORWARD_CHUNKED = 2
 
 KD_NOALLOC_SCRATCH_BYTES = 256 << 20
 
@@ -88,6 +95,17 @@ def _load():
         vp, sz, vp]
     lib.kd_fused_chunked_kl_fwd_noalloc.argtypes = [
         ctypes.c_int, vp, vp, vp, vp, vp, i64, i64, i64, i32, i64, f32, vp, vp, vp, vp, vp]
+    cmp_fwd = [ctypes.c_int, vp, vp, vp, vp, vp, i64, i64, i64, i32, i64, vp, sz, vp, sz, vp, vp, vp, vp]
+    cmp_bwd = [ctypes.c_int, vp, vp, vp, vp, vp, i64, i64, i64, i32, i64, vp, sz, vp, vp, vp, vp, ctypes.c_int,
+               vp, sz, vp]
+    lib.kd_comparator_grid_bytes.argtypes = [ctypes.c_int, i64, i64]
+    lib.kd_comparator_grid_bytes.restype = sz
+    for f in ("kd_dense_kl_fwd", "kd_forward_chunked_kl_fwd"):
+        getattr(lib, f).argtypes = cmp_fwd
+        getattr(lib, f).restype = ctypes.c_int
+    for f in ("kd_dense_kl_bwd", "kd_forward_chunked_kl_bwd"):
+        getattr(lib, f).argtypes = cmp_bwd
+        getattr(lib, f).restype = ctypes.c_int
     lib.kd_status_string.argtypes = [ctypes.c_int]
     lib.kd_status_string.restype = ctypes.c_char_p
     lib.kd_last_error_message.argtypes = []
@@ -251,6 +269,89 @@ def kd_fused_chunked_kl_bwd(H, W, topk_idx, topk_logp, mask, lse, grad_loss=None
         1 if accumulate else 0,
         _ptr(ws), ws.numel() * ws.element_size(), _stream(H.device)))
     return dH, dW
+
+
+def kd_comparator_grid_bytes(variant: int, n: int, V: int) -> int:
+    """Bytes of the grid buffer a comparison variant keeps (KD_VARIANT_DENSE:
+    log q and the teacher grid; KD_VARIANT_FORWARD_CHUNKED: the logits)."""
+    nb = lib().kd_comparator_grid_bytes(variant, n, V)
+    if nb == 0:
+        raise ValueError(f"bad comparator arguments: variant={variant} n={n} V={V}")
+    return nb
+
+
+_CMP = {KD_VARIANT_DENSE: ("kd_dense_kl_fwd", "kd_dense_kl_bwd"),
+        KD_VARIANT_FORWARD_CHUNKED: ("kd_forward_chunked_kl_fwd", "kd_forward_chunked_kl_bwd")}
+
+
+def _comparator_fwd(variant, H, W, topk_idx, topk_logp, mask, chunk, workspace, grid, row_kl, plan):
+    n, d, V, K = _check_inputs(H, W, topk_idx, topk_logp, mask)
+    dt = _dtype_code(H)
+    plan = plan or kd_plan_query(dt, n, d, V, K, chunk)
+    ws = _workspace(plan["fwd_workspace_bytes"], H.device, workspace)
+    gb = kd_comparator_grid_bytes(variant, n, V)
+    grid = _workspace(gb, H.device, grid)
+    loss = torch.empty(1, dtype=torch.float32, device=H.device)
+    lse = torch.empty(n, dtype=torch.float32, device=H.device)
+    rk = torch.empty(n, dtype=torch.float32, device=H.device) if row_kl else None
+    _check(getattr(lib(), _CMP[variant][0])(
+        dt, _ptr(H), _ptr(W), _ptr(topk_idx), _ptr(topk_logp), _ptr(mask), n, d, V, K, plan["chunk"],
+        _ptr(grid), grid.numel() * grid.element_size(), _ptr(ws), ws.numel() * ws.element_size(),
+        _ptr(loss), _ptr(lse), _ptr(rk), _stream(H.device)))
+    return {"loss": loss, "lse": lse, "row_kl": rk, "grid": grid, "plan": plan}
+
+
+def _comparator_bwd(variant, H, W, topk_idx, topk_logp, mask, lse, grid, grad_loss, chunk, workspace, dW,
+                    plan, accumulate):
+    n, d, V, K = _check_inputs(H, W, topk_idx, topk_logp, mask)
+    dt = _dtype_code(H)
+    plan = plan or kd_plan_query(dt, n, d, V, K, chunk)
+    ws = _workspace(plan["bwd_workspace_bytes"], H.device, workspace)
+    if grad_loss is None:
+        grad_loss = torch.ones(1, dtype=torch.float32, device=H.device)
+    grad_loss = grad_loss.reshape(1).to(torch.float32).contiguous()
+    dH = torch.empty_like(H)
+    if dW is None:
+        dW = torch.empty((V, d), dtype=torch.float32, device=H.device)
+        accumulate = False
+    elif dW.dtype != torch.float32 or tuple(dW.shape) != (V, d) or not dW.is_contiguous():
+        raise ValueError("dW must be a contiguous float32 [V, d] tensor")
+    _check(getattr(lib(), _CMP[variant][1])(
+        dt, _ptr(H), _ptr(W), _ptr(topk_idx), _ptr(topk_logp), _ptr(mask), n, d, V, K, plan["chunk"],
+        _ptr(grid), grid.numel() * grid.element_size(), _ptr(lse), _ptr(grad_loss), _ptr(dH), _ptr(dW),
+        1 if accumulate else 0, _ptr(ws), ws.numel() * ws.element_size(), _stream(H.device)))
+    return dH, dW
+
+
+def kd_dense_kl_fwd(H, W, topk_idx, topk_logp, mask=None, chunk: int = 0, workspace=None, grid=None,
+                    row_kl: bool = True, plan: dict | None = None):
+    """Dense-KL forward (comparison variant): builds the full log q and teacher
+    grids in ``grid`` (allocated if not given) and returns loss, lse, row_kl,
+    grid and plan.  The backward needs the same grid, unchanged."""
+    return _comparator_fwd(KD_VARIANT_DENSE, H, W, topk_idx, topk_logp, mask, chunk, workspace, grid,
+                           row_kl, plan)
+
+
+def kd_dense_kl_bwd(H, W, topk_idx, topk_logp, mask, lse, grid, grad_loss=None, chunk: int = 0,
+                    workspace=None, dW=None, plan: dict | None = None, accumulate: bool = True):
+    """Dense-KL backward from the forward's grids: (dH, dW) as kd_fused_chunked_kl_bwd."""
+    return _comparator_bwd(KD_VARIANT_DENSE, H, W, topk_idx, topk_logp, mask, lse, grid, grad_loss, chunk,
+                           workspace, dW, plan, accumulate)
+
+
+def kd_forward_chunked_kl_fwd(H, W, topk_idx, topk_logp, mask=None, chunk: int = 0, workspace=None,
+                              grid=None, row_kl: bool = True, plan: dict | None = None):
+    """Forward-chunked KL forward (comparison variant): the loss chunk by chunk
+    with the logits of every chunk kept in ``grid`` for the backward."""
+    return _comparator_fwd(KD_VARIANT_FORWARD_CHUNKED, H, W, topk_idx, topk_logp, mask, chunk, workspace,
+                           grid, row_kl, plan)
+
+
+def kd_forward_chunked_kl_bwd(H, W, topk_idx, topk_logp, mask, lse, grid, grad_loss=None, chunk: int = 0,
+                              workspace=None, dW=None, plan: dict | None = None, accumulate: bool = True):
+    """Forward-chunked KL backward from the kept logits: (dH, dW)."""
+    return _comparator_bwd(KD_VARIANT_FORWARD_CHUNKED, H, W, topk_idx, topk_logp, mask, lse, grid, grad_loss,
+                           chunk, workspace, dW, plan, accumulate)
 
 
 def kd_teacher_topk_plan(dtype: int, n: int, d: int, V: int, K: int, chunk: int = 0, cap: int = 0,

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkdloss.so")
-SOURCES = ["kd_kernels.hip", "kd_gemm.hip", "kd_topk.hip", "kd_api.cpp"]
+SOURCES = ["kd_kernels.hip", "kd_gemm.hip", "kd_topk.hip", "kd_compare.hip", "kd_api.cpp"]
 ARCH = "gfx950"
 
 

@@ -483,6 +483,219 @@ int run_forward(const Layout& L, const void* H, const void* W, const int32_t* to
   return ok();
 }
 
+// The backward's launch sequence on a planned layout (arguments checked): per
+// chunk the logit gradient G (recomputed from H and W by the fused variant,
+// formed from the forward's stored grids by the comparison variants), dH =
+// G W, and dW (+)= G^T H per pair of chunks.
+enum class Variant { kFused, kDense, kForwardChunked };
+
+int run_backward(const Layout& L, Variant var, const float* grid, const void* H, const void* W,
+                 const int32_t* topk_idx, const float* topk_logp, const uint8_t* mask, float temperature,
+                 const float* lse, const float* grad_loss, void* dH, float* dW, int accumulate_dw,
+                 void* workspace, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  int rc = prepare_teacher(L, topk_idx, topk_logp, mask, temperature, ws, s);
+  if (rc != KD_OK) return rc;
+
+  const size_t es = kd::elem_size(L.dt);
+  const bool w_kmajor = L.dt == DType::BF16;  // dH reads W itself
+  if (!w_kmajor)
+    KD_LAUNCH("transpose_w", 0, 2.0 * L.V * L.d * es,
+              kd::launch_transpose_pad(L.dt, W, (int)L.V, (int)L.d, L.d, ws + L.WT, (int)L.v_pad,
+                                       L.v_pad, s));
+  bool dw_written = accumulate_dw != 0;  // later dW launches accumulate
+  int pair_rows = 0;                      // unpadded rows of the pair's chunks
+  for (int64_t c = 0; c < L.n_chunks; ++c) {
+    const int64_t c0 = c * L.chunk;
+    const int rows = (int)std::min<int64_t>(L.chunk, L.n - c0);
+    const int c_pad = (int)round_up(rows, kd::KPAD);
+    const int col0 = (int)((c % 2) * L.c_pad);  // this chunk's columns in G^T and H^T
+    const char* Hc = static_cast<const char*>(H) + c0 * L.d * es;
+    KD_LAUNCH("transpose_h", 0, 2.0 * rows * L.d * es,
+              kd::launch_transpose_pad(L.dt, Hc, rows, (int)L.d, L.d, ws + L.HT + col0 * es, c_pad,
+                                       L.gt_cols, s));
+    const bool kmajor = L.dt == DType::BF16;  // dW reads G itself
+    const int g_row0 = kmajor ? col0 : 0;
+    kd::RecomputeEpilogue ep{};
+    ep.G = ws + L.G;
+    ep.GT = kmajor ? nullptr : ws + L.GT;
+    ep.g_row0 = g_row0;
+    ep.gt_ld = (int)L.gt_cols;
+    ep.gt_col0 = col0;
+    ep.v_pad = (int)L.v_pad;
+    ep.c_pad = c_pad;
+    ep.c0 = (int)c0;
+    ep.rows = rows;
+    ep.V = (int)L.V;
+    ep.K = (int)L.K;
+    ep.hit_ld = (int)L.n_vt + 1;
+    ep.hit_off = reinterpret_cast<const int*>(ws + L.hit_off);
+    ep.hits = reinterpret_cast<const kd::Hit*>(ws + L.hits);
+    ep.S = reinterpret_cast<const float*>(ws + L.S);
+    ep.lse = lse;
+    ep.mask = mask;
+    ep.ctrl = reinterpret_cast<const kd::Ctrl*>(ws + L.ctrl);
+    ep.grad_loss = grad_loss;
+    ep.tau = temperature;
+    ep.inv_tau = 1.0f / temperature;
+    const double fl = 2.0 * rows * L.d * L.V;
+    if (var == Variant::kFused) {
+      KD_LAUNCH("recompute_gemm", fl,
+                double(L.V) * L.d * es + double(rows) * L.d * es + 2.0 * c_pad * L.v_pad * es,
+                kd::launch_recompute_gemm(L.dt, W, (int)L.V, Hc, rows, (int)L.d, ep, s));
+    } else {
+      // G of this chunk from the grids the forward kept (dense: log q and the
+      // teacher grid; forward-chunked: the logits and the LSE)
+      const long long ldz = L.v_pad;
+      const float* Zc = grid + c0 * ldz;
+      const float* Pc = var == Variant::kDense ? grid + L.n * ldz + c0 * ldz : nullptr;
+      KD_LAUNCH(var == Variant::kDense ? "dense_grad" : "fc_grad", 0,
+                double(rows) * L.V * 4 * (var == Variant::kDense ? 2 : 1) + 2.0 * c_pad * L.v_pad * es,
+                kd::launch_grad_from_grid(var == Variant::kDense, Zc, Pc, ldz, (int)L.V, (int)L.v_pad, rows,
+                                          c_pad, (int)c0, lse, ep.S, mask, ep.ctrl, grad_loss, topk_idx,
+                                          reinterpret_cast<const float*>(ws + L.p), (int)L.K,
+                                          ws + L.G + size_t(g_row0) * L.v_pad * es, s));
+    }
+    const long long split_stride = (long long)L.c_pad * L.d;
+    const size_t dhpart_bytes = L.bwd_end - L.dhpart;
+    if (const char* why = kd::dh_launch_error(L.dt, rows, (int)L.v_pad, (int)L.d, (int)L.splits,
+                                              split_stride, dhpart_bytes))
+      return fail(KD_E_INVAL, "dH launch refused (%d splits, %d rows): %s", (int)L.splits, rows, why);
+    bool launched = false;
+    KD_LAUNCH("dh_gemm", fl,
+              double(c_pad) * L.v_pad * es + double(L.d) * L.v_pad * es + double(L.splits) * rows * L.d * 4,
+              launched = kd::launch_dh_gemm(L.dt, ws + L.G + size_t(g_row0) * L.v_pad * es, rows,
+                                            (int)L.v_pad, w_kmajor ? W : ws + L.WT, w_kmajor, (int)L.V,
+                                            (int)L.d, (int)L.splits, reinterpret_cast<float*>(ws + L.dhpart),
+                                            split_stride, dhpart_bytes, s));
+    if (!launched) return fail(KD_E_INVAL, "dH launch refused by its bounds check");
+    KD_LAUNCH("dh_reduce", 0, double(L.splits) * rows * L.d * 4 + double(rows) * L.d * es,
+              kd::launch_dh_reduce(L.dt, reinterpret_cast<const float*>(ws + L.dhpart),
+                                   (int)L.splits, split_stride, rows, (int)L.d,
+                                   static_cast<char*>(dH) + c0 * L.d * es, s));
+    pair_rows += rows;
+    if (c % 2 == 1 || c == L.n_chunks - 1) {
+      const int k_len = col0 + c_pad;
+      KD_LAUNCH("dw_gemm", 2.0 * pair_rows * L.d * L.V,
+                double(L.V) * k_len * es + double(L.d) * k_len * es +
+                    (dw_written ? 2.0 : 1.0) * L.V * L.d * 4,
+                kmajor ? kd::launch_dw_gemm_kmajor(ws + L.G, (int)L.V, (int)L.v_pad, k_len, L.v_pad,
+                                                   ws + L.HT, (int)L.d, L.gt_cols, dW, dw_written, s)
+                       : kd::launch_dw_gemm(L.dt, ws + L.GT, (int)L.V, k_len, L.gt_cols, ws + L.HT,
+                                            (int)L.d, L.gt_cols, dW, dw_written, s));
+      dw_written = true;
+      pair_rows = 0;
+    }
+  }
+  return ok();
+}
+
+
+// ------------------------------------------------------------------ comparison variants
+// The two other ways the pages compute the same loss, kept to measure the
+// fused variant against on this GPU (aib.vote summary, paragraph comparing
+// Dense KL, Forward-chunked KL and Fused chunked KL): dense KL builds the
+// student's full log-probability grid and the teacher's full probability
+// grid; forward-chunked KL computes the loss chunk by chunk with a sparse
+// teacher but computes and keeps the student's full logit grid for the
+// backward.  Both keep n x V fp32 grids in a caller buffer (pitch v_pad).
+size_t grid_bytes_of(Variant var, int64_t n, int64_t V) {
+  const size_t one = size_t(n) * size_t(round_up(V, kd::KPAD)) * 4;
+  return var == Variant::kDense ? 2 * one : one;
+}
+
+int check_grid(Variant var, const void* grid, size_t grid_bytes, int64_t n, int64_t V) {
+  const size_t need = grid_bytes_of(var, n, V);
+  if (grid == nullptr || grid_bytes < need)
+    return fail(KD_E_WORKSPACE, "grid buffer of %zu bytes needed, %zu given%s", need, grid_bytes,
+                grid == nullptr ? " (null pointer)" : "");
+  if (!aligned16(grid)) return fail(KD_E_INVAL, "the grid buffer must be 16-byte aligned");
+  return KD_OK;
+}
+
+int comparator_fwd(Variant var, int dtype, const void* H, const void* W, const int32_t* topk_idx,
+                   const float* topk_logp, const uint8_t* mask, int64_t n, int64_t d, int64_t V, int32_t K,
+                   int64_t chunk, void* grid, size_t grid_bytes, void* workspace, size_t workspace_bytes,
+                   float* loss, float* lse, float* row_kl, void* stream) {
+  if (dtype != KD_BF16) return fail(KD_E_INVAL, "the comparison variants take bf16 H and W only");
+  Layout L;
+  int rc = plan(dtype, n, d, V, K, chunk, workspace_bytes ? workspace_bytes : 1, &L, Fit::kFwd);
+  if (rc != KD_OK) return rc;
+  if (loss == nullptr || lse == nullptr) return fail(KD_E_INVAL, "loss and lse must be non-null");
+  rc = check_common(H, W, topk_idx, topk_logp, workspace, workspace_bytes, L.fwd_end);
+  if (rc != KD_OK) return rc;
+  rc = check_grid(var, grid, grid_bytes, n, V);
+  if (rc != KD_OK) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  rc = prepare_teacher(L, topk_idx, topk_logp, mask, 1.0f, ws, s);
+  if (rc != KD_OK) return rc;
+  float* rk = row_kl != nullptr ? row_kl : reinterpret_cast<float*>(ws + L.rowkl);
+  const float* p = reinterpret_cast<const float*>(ws + L.p);
+  const long long ldz = L.v_pad;
+  const size_t es = kd::elem_size(L.dt);
+  float* Z = static_cast<float*>(grid);
+  const double grid_row = double(L.V) * 4;
+  if (var == Variant::kDense) {
+    // the whole grids at once, as the dense loss builds them
+    float* P = Z + L.n * ldz;
+    KD_LAUNCH("dense_logits_gemm", 2.0 * L.n * L.d * L.V,
+              double(L.V) * L.d * es + double(L.n) * L.d * es + L.n * grid_row,
+              kd::launch_logits_gemm(L.dt, W, (int)L.V, H, (int)L.n, (int)L.d, Z, ldz, s));
+    KD_LAUNCH("dense_log_softmax", 0, 3.0 * L.n * grid_row,
+              kd::launch_log_softmax(Z, ldz, (int)L.V, (int)L.n, 0, lse, s));
+    KD_LAUNCH("dense_teacher_grid", 0, L.n * grid_row + double(L.n) * L.K * 8,
+              kd::launch_teacher_grid(P, ldz, (int)L.V, (int)L.n, 0, topk_idx, p, mask, (int)L.K, s));
+    KD_LAUNCH("dense_kl", 0, 2.0 * L.n * grid_row,
+              kd::launch_dense_kl(P, Z, ldz, (int)L.V, (int)L.n, 0, mask, rk, s));
+  } else {
+    float* g = reinterpret_cast<float*>(ws + L.g);
+    auto* part = reinterpret_cast<float2*>(ws + L.part);
+    for (int64_t c0 = 0; c0 < L.n; c0 += L.chunk) {
+      const int rows = (int)std::min<int64_t>(L.chunk, L.n - c0);
+      float* Zc = Z + c0 * ldz;
+      const char* Hc = static_cast<const char*>(H) + c0 * L.d * es;
+      KD_LAUNCH("fc_logits_gemm", 2.0 * rows * L.d * L.V,
+                double(L.V) * L.d * es + double(rows) * L.d * es + rows * grid_row,
+                kd::launch_logits_gemm(L.dt, W, (int)L.V, Hc, rows, (int)L.d, Zc, ldz, s));
+      KD_LAUNCH("fc_row_stats", 0, rows * grid_row,
+                kd::launch_row_stats(Zc, ldz, (int)L.V, rows, part, s));
+      KD_LAUNCH("fc_gather", 0, double(rows) * L.K * 12,
+                kd::launch_gather(Zc, ldz, rows, (int)c0, topk_idx, mask, (int)L.K, (int)L.V, g, s));
+      // one (max, sum-exp) "tile" per row
+      KD_LAUNCH("lse_kl", 0, double(rows) * (8 + L.K * 8 + 16),
+                kd::launch_lse_kl(part, (int)L.chunk, 1, (int)c0, rows, p, g,
+                                  reinterpret_cast<const float*>(ws + L.S),
+                                  reinterpret_cast<const float*>(ws + L.E), mask, (int)L.K, 1.0f, lse, rk,
+                                  s));
+    }
+  }
+  KD_LAUNCH("loss", 0, L.n * 4.0,
+            kd::launch_loss(rk, (int)L.n, reinterpret_cast<const kd::Ctrl*>(ws + L.ctrl), loss, s));
+  return ok();
+}
+
+int comparator_bwd(Variant var, int dtype, const void* H, const void* W, const int32_t* topk_idx,
+                   const float* topk_logp, const uint8_t* mask, int64_t n, int64_t d, int64_t V, int32_t K,
+                   int64_t chunk, const void* grid, size_t grid_bytes, const float* lse,
+                   const float* grad_loss, void* dH, float* dW, int accumulate_dw, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  if (dtype != KD_BF16) return fail(KD_E_INVAL, "the comparison variants take bf16 H and W only");
+  Layout L;
+  int rc = plan(dtype, n, d, V, K, chunk, workspace_bytes ? workspace_bytes : 1, &L, Fit::kBwd);
+  if (rc != KD_OK) return rc;
+  if (lse == nullptr || grad_loss == nullptr || dH == nullptr || dW == nullptr)
+    return fail(KD_E_INVAL, "lse, grad_loss, dH and dW must be non-null");
+  if (!aligned16(dH) || !aligned16(dW)) return fail(KD_E_INVAL, "dH and dW must be 16-byte aligned");
+  rc = check_common(H, W, topk_idx, topk_logp, workspace, workspace_bytes, L.bwd_end);
+  if (rc != KD_OK) return rc;
+  rc = check_grid(var, grid, grid_bytes, n, V);
+  if (rc != KD_OK) return rc;
+  return run_backward(L, var, static_cast<const float*>(grid), H, W, topk_idx, topk_logp, mask, 1.0f, lse,
+                      grad_loss, dH, dW, accumulate_dw, workspace, stream);
+}
+
 // ------------------------------------------------------------------ no-allocation forward
 // The workspace of kd_fused_chunked_kl_fwd_noalloc: a file-scope device array,
 // one per GPU the library runs on, held until the process ends.  Host code
@@ -646,88 +859,49 @@ int kd_fused_chunked_kl_bwd(int dtype, const void* H, const void* W, const int32
   if (rc != KD_OK) return rc;
   rc = check_common(H, W, topk_idx, topk_logp, workspace, workspace_bytes, L.bwd_end);
   if (rc != KD_OK) return rc;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  rc = prepare_teacher(L, topk_idx, topk_logp, mask, temperature, ws, s);
-  if (rc != KD_OK) return rc;
+  return run_backward(L, Variant::kFused, nullptr, H, W, topk_idx, topk_logp, mask, temperature, lse,
+                      grad_loss, dH, dW, accumulate_dw, workspace, stream);
+}
 
-  const size_t es = kd::elem_size(L.dt);
-  const bool w_kmajor = L.dt == DType::BF16;  // dH reads W itself
-  if (!w_kmajor)
-    KD_LAUNCH("transpose_w", 0, 2.0 * L.V * L.d * es,
-              kd::launch_transpose_pad(L.dt, W, (int)L.V, (int)L.d, L.d, ws + L.WT, (int)L.v_pad,
-                                       L.v_pad, s));
-  bool dw_written = accumulate_dw != 0;  // later dW launches accumulate
-  int pair_rows = 0;                      // unpadded rows of the pair's chunks
-  for (int64_t c = 0; c < L.n_chunks; ++c) {
-    const int64_t c0 = c * L.chunk;
-    const int rows = (int)std::min<int64_t>(L.chunk, L.n - c0);
-    const int c_pad = (int)round_up(rows, kd::KPAD);
-    const int col0 = (int)((c % 2) * L.c_pad);  // this chunk's columns in G^T and H^T
-    const char* Hc = static_cast<const char*>(H) + c0 * L.d * es;
-    KD_LAUNCH("transpose_h", 0, 2.0 * rows * L.d * es,
-              kd::launch_transpose_pad(L.dt, Hc, rows, (int)L.d, L.d, ws + L.HT + col0 * es, c_pad,
-                                       L.gt_cols, s));
-    const bool kmajor = L.dt == DType::BF16;  // dW reads G itself
-    const int g_row0 = kmajor ? col0 : 0;
-    kd::RecomputeEpilogue ep{};
-    ep.G = ws + L.G;
-    ep.GT = kmajor ? nullptr : ws + L.GT;
-    ep.g_row0 = g_row0;
-    ep.gt_ld = (int)L.gt_cols;
-    ep.gt_col0 = col0;
-    ep.v_pad = (int)L.v_pad;
-    ep.c_pad = c_pad;
-    ep.c0 = (int)c0;
-    ep.rows = rows;
-    ep.V = (int)L.V;
-    ep.K = (int)L.K;
-    ep.hit_ld = (int)L.n_vt + 1;
-    ep.hit_off = reinterpret_cast<const int*>(ws + L.hit_off);
-    ep.hits = reinterpret_cast<const kd::Hit*>(ws + L.hits);
-    ep.S = reinterpret_cast<const float*>(ws + L.S);
-    ep.lse = lse;
-    ep.mask = mask;
-    ep.ctrl = reinterpret_cast<const kd::Ctrl*>(ws + L.ctrl);
-    ep.grad_loss = grad_loss;
-    ep.tau = temperature;
-    ep.inv_tau = 1.0f / temperature;
-    const double fl = 2.0 * rows * L.d * L.V;
-    KD_LAUNCH("recompute_gemm", fl,
-              double(L.V) * L.d * es + double(rows) * L.d * es + 2.0 * c_pad * L.v_pad * es,
-              kd::launch_recompute_gemm(L.dt, W, (int)L.V, Hc, rows, (int)L.d, ep, s));
-    const long long split_stride = (long long)L.c_pad * L.d;
-    const size_t dhpart_bytes = L.bwd_end - L.dhpart;
-    if (const char* why = kd::dh_launch_error(L.dt, rows, (int)L.v_pad, (int)L.d, (int)L.splits,
-                                              split_stride, dhpart_bytes))
-      return fail(KD_E_INVAL, "dH launch refused (%d splits, %d rows): %s", (int)L.splits, rows, why);
-    bool launched = false;
-    KD_LAUNCH("dh_gemm", fl,
-              double(c_pad) * L.v_pad * es + double(L.d) * L.v_pad * es + double(L.splits) * rows * L.d * 4,
-              launched = kd::launch_dh_gemm(L.dt, ws + L.G + size_t(g_row0) * L.v_pad * es, rows,
-                                            (int)L.v_pad, w_kmajor ? W : ws + L.WT, w_kmajor, (int)L.V,
-                                            (int)L.d, (int)L.splits, reinterpret_cast<float*>(ws + L.dhpart),
-                                            split_stride, dhpart_bytes, s));
-    if (!launched) return fail(KD_E_INVAL, "dH launch refused by its bounds check");
-    KD_LAUNCH("dh_reduce", 0, double(L.splits) * rows * L.d * 4 + double(rows) * L.d * es,
-              kd::launch_dh_reduce(L.dt, reinterpret_cast<const float*>(ws + L.dhpart),
-                                   (int)L.splits, split_stride, rows, (int)L.d,
-                                   static_cast<char*>(dH) + c0 * L.d * es, s));
-    pair_rows += rows;
-    if (c % 2 == 1 || c == L.n_chunks - 1) {
-      const int k_len = col0 + c_pad;
-      KD_LAUNCH("dw_gemm", 2.0 * pair_rows * L.d * L.V,
-                double(L.V) * k_len * es + double(L.d) * k_len * es +
-                    (dw_written ? 2.0 : 1.0) * L.V * L.d * 4,
-                kmajor ? kd::launch_dw_gemm_kmajor(ws + L.G, (int)L.V, (int)L.v_pad, k_len, L.v_pad,
-                                                   ws + L.HT, (int)L.d, L.gt_cols, dW, dw_written, s)
-                       : kd::launch_dw_gemm(L.dt, ws + L.GT, (int)L.V, k_len, L.gt_cols, ws + L.HT,
-                                            (int)L.d, L.gt_cols, dW, dw_written, s));
-      dw_written = true;
-      pair_rows = 0;
-    }
-  }
-  return ok();
+size_t kd_comparator_grid_bytes(int variant, int64_t n, int64_t V) {
+  if (n <= 0 || V <= 0) return 0;
+  if (variant == KD_VARIANT_DENSE) return grid_bytes_of(Variant::kDense, n, V);
+  if (variant == KD_VARIANT_FORWARD_CHUNKED) return grid_bytes_of(Variant::kForwardChunked, n, V);
+  return 0;
+}
+
+int kd_dense_kl_fwd(int dtype, const void* H, const void* W, const int32_t* topk_idx, const float* topk_logp,
+                    const uint8_t* mask, int64_t n, int64_t d, int64_t V, int32_t K, int64_t chunk, void* grid,
+                    size_t grid_bytes, void* workspace, size_t workspace_bytes, float* loss, float* lse,
+                    float* row_kl, void* stream) {
+  return comparator_fwd(Variant::kDense, dtype, H, W, topk_idx, topk_logp, mask, n, d, V, K, chunk, grid,
+                        grid_bytes, workspace, workspace_bytes, loss, lse, row_kl, stream);
+}
+
+int kd_dense_kl_bwd(int dtype, const void* H, const void* W, const int32_t* topk_idx, const float* topk_logp,
+                    const uint8_t* mask, int64_t n, int64_t d, int64_t V, int32_t K, int64_t chunk,
+                    const void* grid, size_t grid_bytes, const float* lse, const float* grad_loss, void* dH,
+                    float* dW, int accumulate_dw, void* workspace, size_t workspace_bytes, void* stream) {
+  return comparator_bwd(Variant::kDense, dtype, H, W, topk_idx, topk_logp, mask, n, d, V, K, chunk, grid,
+                        grid_bytes, lse, grad_loss, dH, dW, accumulate_dw, workspace, workspace_bytes, stream);
+}
+
+int kd_forward_chunked_kl_fwd(int dtype, const void* H, const void* W, const int32_t* topk_idx,
+                              const float* topk_logp, const uint8_t* mask, int64_t n, int64_t d, int64_t V,
+                              int32_t K, int64_t chunk, void* grid, size_t grid_bytes, void* workspace,
+                              size_t workspace_bytes, float* loss, float* lse, float* row_kl, void* stream) {
+  return comparator_fwd(Variant::kForwardChunked, dtype, H, W, topk_idx, topk_logp, mask, n, d, V, K, chunk,
+                        grid, grid_bytes, workspace, workspace_bytes, loss, lse, row_kl, stream);
+}
+
+int kd_forward_chunked_kl_bwd(int dtype, const void* H, const void* W, const int32_t* topk_idx,
+                              const float* topk_logp, const uint8_t* mask, int64_t n, int64_t d, int64_t V,
+                              int32_t K, int64_t chunk, const void* grid, size_t grid_bytes, const float* lse,
+                              const float* grad_loss, void* dH, float* dW, int accumulate_dw, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  return comparator_bwd(Variant::kForwardChunked, dtype, H, W, topk_idx, topk_logp, mask, n, d, V, K, chunk,
+                        grid, grid_bytes, lse, grad_loss, dH, dW, accumulate_dw, workspace, workspace_bytes,
+                        stream);
 }
 
 int kd_teacher_topk_plan(int dtype, int64_t n, int64_t d, int64_t V, int32_t K, int64_t chunk,

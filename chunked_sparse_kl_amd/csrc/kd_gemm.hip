@@ -223,6 +223,7 @@ struct MainLoop {
   static constexpr int EPC = 16 / sizeof(T);      // elements per 16-byte chunk
   static constexpr int WAVES = 2 * WC;            // 2 wavefront rows x WC columns
   static constexpr int ROWS_PER_LD = 8 * WAVES;   // staged rows written by one instruction index
+  static constexpr int KROWS_PER_LD = 2 * WAVES;  // k-major: k rows (of BM / BN elements) per instruction index
   static constexpr int A_LD = BM / ROWS_PER_LD;   // per-wavefront load instructions per K block (A)
   static constexpr int B_LD = BN / ROWS_PER_LD;
   static constexpr int LOADS = A_LD + B_LD;
@@ -253,7 +254,7 @@ struct MainLoop {
     c = (lane & 7) ^ (((wave_row + r) >> 1) & 7);
     k_elems = ke;
     if constexpr (kAT) {
-      // A.rows is the m extent; lane L of load i stages k row 16 i + 2 w + L / 32,
+      // A.rows is the m extent; lane L of load i stages k row 2 WAVES i + 2 w + L / 32,
       // physical chunk L % 32, i.e. logical chunk (L % 32) ^ 4 (row % 4).
       const int row = 2 * w + (lane >> 5);
       const int ca = (lane & 31) ^ (4 * (row & 3));
@@ -261,7 +262,7 @@ struct MainLoop {
       a_tile = A.base + (long long)tm * BM * (long long)sizeof(T);
       a_ld = A.ld;
       a_off = (ca * EPC < a_valid) ? (unsigned)(row * A.ld + ca * 16) : kOut;
-      a_step = (unsigned)(16 * A.ld);
+      a_step = (unsigned)(KROWS_PER_LD * A.ld);
       b_valid = min(B.rows - tn * BN, BN);
       b_tile = B.base + (long long)tn * BN * B.ld;
       b_bytes = (unsigned)(b_valid * B.ld);
@@ -278,7 +279,7 @@ struct MainLoop {
     a_off = (unsigned)((wave_row + r) * A.ld + c * 16);
     a_step = (unsigned)(ROWS_PER_LD * A.ld);
     if constexpr (kBT) {
-      // as k-major A: lane L of load i stages k row 16 i + 2 w + L / 32 of
+      // as k-major A: lane L of load i stages k row 2 WAVES i + 2 w + L / 32 of
       // the block, logical chunk (L % 32) ^ 4 (row % 4) of its BN columns
       static_assert(BN == BM && B_LD == A_LD, "k-major B staging mirrors k-major A");
       const int row = 2 * w + (lane >> 5);
@@ -287,7 +288,7 @@ struct MainLoop {
       b_ldk = B.ld;
       b_krows = B.krows;
       b_off = (cb * EPC < b_valid) ? (unsigned)(row * B.ld + cb * 16) : kOut;
-      b_step = (unsigned)(16 * B.ld);
+      b_step = (unsigned)(KROWS_PER_LD * B.ld);
       return;
     }
     b_tile = B.base + (long long)tn * BN * B.ld;
@@ -305,7 +306,7 @@ struct MainLoop {
     if constexpr (kAT) {
       const i32x4 rk = make_rsrc(a_tile + (long long)kb * BK * a_ld, (unsigned)(BK * a_ld));
       const unsigned off = (valid && a_off != kOut) ? a_off + i * a_step : kOut;
-      dma16(rk, off, __builtin_amdgcn_readfirstlane(lds_addr(st + (16 * i + wave_row / 4) * BM * (int)sizeof(T))));
+      dma16(rk, off, __builtin_amdgcn_readfirstlane(lds_addr(st + (KROWS_PER_LD * i + wave_row / 4) * BM * (int)sizeof(T))));
       return;
     }
     const unsigned off = (valid && wave_row + r + ROWS_PER_LD * i < a_valid) ? a_off + i * a_step + (unsigned)kb * ROWB : kOut;
@@ -317,7 +318,7 @@ struct MainLoop {
       const int rows_here = max(0, min(BK, b_krows - k0));  // k rows of this block in memory
       const i32x4 rk = make_rsrc(b_tile + (long long)k0 * b_ldk, (unsigned)(rows_here * b_ldk));
       const unsigned off = (valid && b_off != kOut) ? b_off + i * b_step : kOut;
-      dma16(rk, off, __builtin_amdgcn_readfirstlane(lds_addr(st + (16 * i + wave_row / 4) * BN * (int)sizeof(T))));
+      dma16(rk, off, __builtin_amdgcn_readfirstlane(lds_addr(st + (KROWS_PER_LD * i + wave_row / 4) * BN * (int)sizeof(T))));
       return;
     }
     const unsigned off = (valid && wave_row + r + ROWS_PER_LD * i < b_valid) ? b_off + i * b_step + (unsigned)kb * ROWB : kOut;
@@ -877,6 +878,47 @@ __global__ __launch_bounds__(kFusedThreads, 1) void recompute_gemm_kernel(Operan
   }
 }
 
+// ------------------------------------------------------------------ logits (comparators)
+// D[v][t] = z_{t,v}, stored as it is: Z[t][v] in fp32 (row pitch ldz floats,
+// a multiple of 4) for the comparison variants that keep the logits.  For a
+// fixed register group a lane holds 4 consecutive vocabulary rows of one
+// token, stored as one 16-byte vector (element by element at the V end).
+template <typename T>
+__global__ __launch_bounds__(kFusedThreads, 1) void logits_gemm_kernel(Operand A, Operand B, int k_elems,
+                                                                        int tiles_m, int tiles_n, float* Z,
+                                                                        long long ldz, int V, int rows) {
+  constexpr int BN = 256, NBJ = kFusedNBJ, WC = kFusedWC;
+  KD_DECLARE_LDS(BN);
+  const TileIdx ti = map_tile<4>(tiles_m, tiles_n, 1);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave / WC, wc = wave % WC, r32 = lane & 31, h = lane >> 5;
+  f32x16 acc[4][NBJ];
+  const int kb_end = (k_elems + Traits<T>::BK - 1) / Traits<T>::BK;
+  gemm_mainloop<T, BN, WC>(A, B, k_elems, ti.tm, ti.tn, 0, kb_end, lds, acc);
+  const int v_wave = ti.tm * BM + wr * 128;
+#pragma unroll
+  for (int bj = 0; bj < NBJ; ++bj) {
+    const int t = ti.tn * BN + wc * 64 + bj * 32 + r32;
+    float* const zr = Z + (long long)t * ldz;
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int v = v_wave + bi * 32 + 8 * i + 4 * h;
+        if (t >= rows) continue;
+        if (v + 3 < V) {
+          *reinterpret_cast<f32x4*>(zr + v) = f32x4{acc[bi][bj][4 * i], acc[bi][bj][4 * i + 1],
+                                                   acc[bi][bj][4 * i + 2], acc[bi][bj][4 * i + 3]};
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (v + j < V) zr[v + j] = acc[bi][bj][4 * i + j];
+        }
+      }
+  }
+}
+
 // ------------------------------------------------------------------ top-K candidates
 // D[v][t] = z_{t,v}, the same main loop as the forward statistics pass, so the
 // logits are bitwise those whose tile maxima set the thresholds.  Each logit
@@ -1040,6 +1082,14 @@ void recompute_impl(const void* W, int V, const void* Hc, int rows, int d,
 }
 
 template <typename T>
+void logits_impl(const void* W, int V, const void* Hc, int rows, int d, float* Z, long long ldz,
+                 hipStream_t s) {
+  const int tiles_m = (V + BM - 1) / BM, tiles_n = (rows + 255) / 256;
+  logits_gemm_kernel<T><<<tiles_m * tiles_n, kFusedThreads, 0, s>>>(
+      make_operand<T>(W, d, V), make_operand<T>(Hc, d, rows), d, tiles_m, tiles_n, Z, ldz, V, rows);
+}
+
+template <typename T>
 void topk_cand_impl(const void* Wt, int V, const void* Hc, int rows, int d, const CandEpilogue& ep,
                     hipStream_t s) {
   const int tiles_m = (V + BM - 1) / BM, tiles_n = (rows + 255) / 256;
@@ -1055,6 +1105,14 @@ void launch_topk_cand_gemm(DType t, const void* Wt, int V, const void* Hc, int r
     topk_cand_impl<__bf16>(Wt, V, Hc, rows, d, ep, s);
   else
     topk_cand_impl<float>(Wt, V, Hc, rows, d, ep, s);
+}
+
+void launch_logits_gemm(DType t, const void* W, int V, const void* Hc, int rows, int d, float* Z,
+                        long long ldz, hipStream_t s) {
+  if (t == DType::BF16)
+    logits_impl<__bf16>(W, V, Hc, rows, d, Z, ldz, s);
+  else
+    logits_impl<float>(W, V, Hc, rows, d, Z, ldz, s);
 }
 
 void launch_fwd_gemm(DType t, const void* W, int V, const void* Hc, int rows, int d,

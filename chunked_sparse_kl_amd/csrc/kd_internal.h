@@ -32,7 +32,8 @@ enum class DType { BF16 = 0, F32 = 1 };
 // One unmasked teacher entry (row, k), bucketed by (vocabulary tile, 64-row
 // block): its row, k, vocabulary id and the probability its scatter
 // subtracts: p_{row,k}, or for an id the row repeats, the sum of the p of all
-// its occurrences at the first one (in k order) and 0 at the others.
+// its occurrences at the first one (in k order) and 0 at the others (the
+// workspace's p array holds the same values).
 struct alignas(16) Hit {
   int row;
   int k;
@@ -51,7 +52,7 @@ void launch_fill_i32(int* p, long long count, int value, hipStream_t s);
 // (row block rb, vocabulary tile j) holds the unmasked entries of rb whose id
 // lies in tile j, at hits[hit_off[rb * (n_vt + 1) + j] .. hit_off[... + j + 1]);
 // row block rb owns the hit range [rb * 64 * K, (rb + 1) * 64 * K).
-constexpr int kMaxVocabTiles = 16383;  // LDS bucket counters of one workgroup (64 KB)
+constexpr int kMaxVocabTiles = 13307;  // LDS of one workgroup: bucket counters and repeated-id tables (64 KB)
 void launch_teacher_bucket(const float* logp, const int* idx, const uint8_t* mask, int n, int K,
                            int V, float inv_tau, float* p, float* S, float* E, int* hit_off,
                            Hit* hits, Ctrl* ctrl, hipStream_t s);
@@ -133,6 +134,31 @@ void launch_dw_gemm(DType t, const void* GT, int V, int k_len, long long ld_gt, 
 // dW[V][d] (+)= G^T * H.
 void launch_dw_gemm_kmajor(const void* G, int V, int v_pad, int k_len, long long ld_g, const void* HT,
                            int d, long long ld_ht, float* dW, bool accumulate, hipStream_t s);
+
+// ---------------------------------------------------------------- comparison variants (dense, forward-chunked)
+// Z[t][v] = logits of rows [0, rows) of Hc in fp32 (row pitch ldz floats, a
+// multiple of 4; 16-byte aligned Z).
+void launch_logits_gemm(DType t, const void* W, int V, const void* Hc, int rows, int d, float* Z,
+                        long long ldz, hipStream_t s);
+// part[r] = (max, sum-exp) of logit row r.
+void launch_row_stats(const float* Z, long long ldz, int V, int rows, float2* part, hipStream_t s);
+// In place: row r -> z - LSE(z); lse[c0 + r] = LSE(z).
+void launch_log_softmax(float* Z, long long ldz, int V, int rows, int c0, float* lse, hipStream_t s);
+// Dense teacher grid rows: p at the rows' ids, 0 elsewhere.
+void launch_teacher_grid(float* P, long long ldz, int V, int rows, int c0, const int* idx, const float* p,
+                         const uint8_t* mask, int K, hipStream_t s);
+// row_kl[c0 + r] = sum_v P (log P - log q).
+void launch_dense_kl(const float* P, const float* LQ, long long ldz, int V, int rows, int c0, const uint8_t* mask,
+                     float* row_kl, hipStream_t s);
+// g[c0 + r][k] = Z[r][i_{c0+r,k}].
+void launch_gather(const float* Z, long long ldz, int rows, int c0, const int* idx, const uint8_t* mask, int K,
+                   int V, float* g, hipStream_t s);
+// bf16 G rows [0, c_pad) (pitch v_pad) of one chunk from stored grids: dense
+// (Z = log q, P = teacher grid) or forward-chunked (Z = logits, lse).
+void launch_grad_from_grid(bool dense, const float* Z, const float* P, long long ldz, int V, int v_pad, int rows,
+                           int c_pad, int c0, const float* lse, const float* S, const uint8_t* mask,
+                           const Ctrl* ctrl, const float* grad_loss, const int* idx, const float* p, int K,
+                           void* G, hipStream_t s);
 
 // ---------------------------------------------------------------- teacher top-K cache builder
 struct CandEpilogue {

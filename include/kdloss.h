@@ -168,6 +168,54 @@ int kd_fused_chunked_kl_bwd(int dtype, const void* H, const void* W, const int32
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Comparison variants: the two other ways the pages compute this same loss
+ * (aib.vote summary, paragraph comparing Dense KL, Forward-chunked KL and
+ * Fused chunked KL; Hugging Face blog "Making Knowledge Distillation Cheap
+ * Enough to Run at Scale", sections "Two systems changes" and "Scaling to
+ * long context lengths"), built to measure the fused calls against on the
+ * same GPU.  They keep n x V fp32 grids, so their memory grows with n x V:
+ *   dense KL:           the forward builds the student's full log-probability
+ *                       grid log q [n, V] and the teacher's full probability
+ *                       grid P [n, V] (p at the cached ids, 0 elsewhere) and
+ *                       takes KL_t = sum_v P (log P - log q); the backward
+ *                       forms G = gw (S_t exp(log q) - P) from the two grids;
+ *   forward-chunked KL: the forward computes each chunk's logits, keeps them
+ *                       all in a logit grid Z [n, V] and takes the loss with
+ *                       the sparse teacher, as the fused forward does; the
+ *                       backward forms G from the kept logits and the LSE
+ *                       instead of recomputing them.
+ * Both then run the fused backward's dH = G W and dW (+)= G^T H per chunk.
+ * Arguments are those of the fused calls (temperature 1, bf16 H and W only:
+ * KD_E_INVAL otherwise), plus the grid buffer: caller-owned device memory of
+ * at least kd_comparator_grid_bytes(variant, n, V) bytes, 16-byte aligned,
+ * written by the forward and read by the backward, which must get it
+ * unchanged.  The workspace is the fused calls' (plan.fwd_workspace_bytes /
+ * plan.bwd_workspace_bytes).  Results equal the fused calls' up to rounding,
+ * except that the dense grid sums an id a row repeats before taking its
+ * entropy term p log p (the sparse form keeps one term per entry).
+ */
+enum { KD_VARIANT_DENSE = 1, KD_VARIANT_FORWARD_CHUNKED = 2 };
+/* Bytes of the grid buffer (dense: 2 grids, forward-chunked: 1); 0 for bad arguments. */
+size_t kd_comparator_grid_bytes(int variant, int64_t n, int64_t V);
+int kd_dense_kl_fwd(int dtype, const void* H, const void* W, const int32_t* topk_idx, const float* topk_logp,
+                    const uint8_t* mask, int64_t n, int64_t d, int64_t V, int32_t K, int64_t chunk, void* grid,
+                    size_t grid_bytes, void* workspace, size_t workspace_bytes, float* loss, float* lse,
+                    float* row_kl, void* stream);
+int kd_dense_kl_bwd(int dtype, const void* H, const void* W, const int32_t* topk_idx, const float* topk_logp,
+                    const uint8_t* mask, int64_t n, int64_t d, int64_t V, int32_t K, int64_t chunk,
+                    const void* grid, size_t grid_bytes, const float* lse, const float* grad_loss, void* dH,
+                    float* dW, int accumulate_dw, void* workspace, size_t workspace_bytes, void* stream);
+int kd_forward_chunked_kl_fwd(int dtype, const void* H, const void* W, const int32_t* topk_idx,
+                              const float* topk_logp, const uint8_t* mask, int64_t n, int64_t d, int64_t V,
+                              int32_t K, int64_t chunk, void* grid, size_t grid_bytes, void* workspace,
+                              size_t workspace_bytes, float* loss, float* lse, float* row_kl, void* stream);
+int kd_forward_chunked_kl_bwd(int dtype, const void* H, const void* W, const int32_t* topk_idx,
+                              const float* topk_logp, const uint8_t* mask, int64_t n, int64_t d, int64_t V,
+                              int32_t K, int64_t chunk, const void* grid, size_t grid_bytes, const float* lse,
+                              const float* grad_loss, void* dH, float* dW, int accumulate_dw, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/*
  * Teacher top-K cache builder: the offline cache the loss above consumes.
  * The pages keep, for every position, the K most likely tokens of the
  * teacher, computed once (Hugging Face blog "Making Knowledge Distillation

@@ -179,3 +179,28 @@ def test_auto_chunk_calls_plan_against_their_own_workspace(n, d, V, K):
     rc = lib.kd_fused_chunked_kl_fwd(0, fake, fake, fake, fake, None, n, d, V, K, 0, 1.0, fake,
                                      small["fwd_workspace_bytes"] - 1, None, fake, None, None, None)
     assert rc == -2 and b"bytes" in lib.kd_last_error_message()
+
+
+def test_comparator_grid_bytes_and_refusals_without_device_work():
+    lib = kd.lib()
+    n, V = 32768, 201088
+    one = n * (-(-V // 64) * 64) * 4
+    assert kd.kd_comparator_grid_bytes(kd.KD_VARIANT_DENSE, n, V) == 2 * one
+    assert kd.kd_comparator_grid_bytes(kd.KD_VARIANT_FORWARD_CHUNKED, n, V) == one
+    assert lib.kd_comparator_grid_bytes(3, n, V) == 0 and lib.kd_comparator_grid_bytes(1, 0, V) == 0
+    fake = ctypes.c_void_p(4096)
+    p = kd.kd_plan_query(kd.KD_BF16, 256, 256, 4096, 16, 64, 0)
+    for fwd in (lib.kd_dense_kl_fwd, lib.kd_forward_chunked_kl_fwd):
+        # a grid one byte short
+        need = lib.kd_comparator_grid_bytes(1 if fwd is lib.kd_dense_kl_fwd else 2, 256, 4096)
+        rc = fwd(0, fake, fake, fake, fake, None, 256, 256, 4096, 16, 64, fake, need - 1, fake,
+                 p["fwd_workspace_bytes"], fake, fake, None, None)
+        assert rc == -2 and b"grid" in lib.kd_last_error_message()
+        # fp32 inputs
+        rc = fwd(1, fake, fake, fake, fake, None, 256, 256, 4096, 16, 64, fake, need, fake,
+                 p["fwd_workspace_bytes"], fake, fake, None, None)
+        assert rc == -1 and b"bf16" in lib.kd_last_error_message()
+    for bwd in (lib.kd_dense_kl_bwd, lib.kd_forward_chunked_kl_bwd):
+        rc = bwd(0, fake, fake, fake, fake, None, 256, 256, 4096, 16, 64, None, 0, fake, fake, fake, fake, 0,
+                 fake, p["bwd_workspace_bytes"], None)
+        assert rc == -2 and b"grid" in lib.kd_last_error_message()

@@ -16,7 +16,7 @@ import pytest
 from chunked_sparse_kl_amd import build as B
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-KERNEL_OBJS = ["kd_kernels.o", "kd_gemm.o", "kd_topk.o"]
+KERNEL_OBJS = ["kd_kernels.o", "kd_gemm.o", "kd_topk.o", "kd_compare.o"]
 SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
        "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
 
