@@ -83,6 +83,29 @@ int main() {
                          nullptr),
          KD_E_INVAL, "topk null Ht");
 
+  // comparison variants: grid sizes, refusals before any device work
+  if (kd_comparator_grid_bytes(KD_VARIANT_DENSE, 256, 4096) != 2 * kd_comparator_grid_bytes(KD_VARIANT_FORWARD_CHUNKED, 256, 4096) ||
+      kd_comparator_grid_bytes(3, 256, 4096) != 0 || kd_comparator_grid_bytes(KD_VARIANT_DENSE, 0, 4096) != 0) {
+    std::printf("FAIL comparator grid bytes\n");
+    g_fail = 1;
+  }
+  expect(kd_dense_kl_fwd(KD_F32, dummy, dummy, idx, dummy, nullptr, 256, 256, 4096, 16, 64, ws, sizeof(ws), ws,
+                         sizeof(ws), dummy, dummy, nullptr, nullptr),
+         KD_E_INVAL, "dense fwd fp32");
+  expect(kd_forward_chunked_kl_fwd(KD_BF16, dummy, dummy, idx, dummy, nullptr, 256, 256, 4096, 16, 64, ws,
+                                   sizeof(ws), ws, sizeof(ws), dummy, dummy, nullptr, nullptr),
+         KD_E_WORKSPACE, "forward-chunked fwd small workspace");
+  expect(kd_dense_kl_bwd(KD_BF16, dummy, dummy, idx, dummy, nullptr, 256, 256, 4096, 16, 64, nullptr, 0, dummy,
+                         dummy, dummy, dummy, 0, ws, sizeof(ws), nullptr),
+         KD_E_WORKSPACE, "dense bwd small workspace");
+  // the no-allocation forward: a problem beyond its scratch is refused before any device work
+  expect(kd_fused_chunked_kl_fwd_noalloc(KD_BF16, dummy, dummy, idx, dummy, nullptr, 262144, 3072, 128256, 100, 0,
+                                         1.f, dummy, dummy, nullptr, nullptr, nullptr),
+         KD_E_WORKSPACE, "no-alloc fwd beyond scratch");
+  expect(kd_fused_chunked_kl_fwd_noalloc(KD_BF16, dummy, dummy, idx, dummy, nullptr, 256, 256, 4096, 16, 64, 1.f,
+                                         nullptr, dummy, nullptr, nullptr, nullptr),
+         KD_E_INVAL, "no-alloc fwd null loss");
+
   // status strings, validation switch, timing records
   for (int s = -6; s <= 2; ++s)
     if (kd_status_string(s) == nullptr || std::strlen(kd_status_string(s)) == 0) {
