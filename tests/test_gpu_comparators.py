@@ -53,6 +53,14 @@ def test_variant_matches_oracle_small_ragged(name, chunk):
 
 
 @pytest.mark.parametrize("name", sorted(VARIANTS))
+def test_variant_odd_vocabulary(name):
+    # V = 1001: the logit rows end inside a 16-byte vector (element-wise stores
+    # at the end of each row) and inside the last 256-wide vocabulary tile
+    inp = synth.make_custom(333, 136, 1001, 9, "bf16", "random5", "uniform", seed=46)
+    check_full(inp, run_variant(name, inp, chunk=128, grad=1.1), "bf16", grad=1.1)
+
+
+@pytest.mark.parametrize("name", sorted(VARIANTS))
 def test_variant_below_one_tile(name):
     inp = synth.make_custom(70, 40, 100, 7, "bf16", "random5", "uniform", seed=42)
     check_full(inp, run_variant(name, inp), "bf16")
