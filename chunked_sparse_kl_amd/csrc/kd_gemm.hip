@@ -792,20 +792,38 @@ __global__ __launch_bounds__(kFusedThreads, 1) void recompute_gemm_kernel(Operan
   const int nv = ep.ctrl->n_valid;
   const float gw = nv > 0 ? ep.tau * ep.grad_loss[0] / (float)nv : 0.f;
   const float sc = kLog2e * ep.inv_tau;
+  // bf16 G: coef * 2^(z sc - lse2) with coef = gw S_t (S_t >= 0, so coef has
+  // gw's sign) is formed as sign(gw) * 2^(z sc - (lse2 - log2 |coef|)): one FMA
+  // and one exp per element, no multiply and no select.  Its magnitude is off
+  // by a few fp32 ulps, far below the rounding to bf16.  A row without gradient
+  // (masked, past the chunk end, or coef = 0) gets the offset +inf and so
+  // 2^-inf = 0 everywhere.  The teacher entries below are applied to the
+  // magnitude and the sign comes last.  fp32 G keeps the product form.
+  constexpr bool kLogScale = sizeof(T) == 2;
 #pragma unroll
   for (int bj = 0; bj < NBJ; ++bj) {
     const int n = n_wave + bj * 32 + r32;
     const int t = ep.c0 + n;
     const bool live = n < ep.rows && (ep.mask == nullptr || ep.mask[t] != 0);
-    const float coef = live ? gw * ep.S[t] : 0.f;
-    const float lse2 = live ? ep.lse[t] * kLog2e : 0.f;
+    if constexpr (kLogScale) {
+      const float mag = live ? fabsf(gw) * ep.S[t] : 0.f;
+      const float off = mag > 0.f ? ep.lse[t] * kLog2e - __builtin_amdgcn_logf(mag) : __builtin_inff();
 #pragma unroll
-    for (int bi = 0; bi < 4; ++bi)
+      for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float q = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[bi][bj][e], sc, -lse2));
-        acc[bi][bj][e] = live ? coef * q : 0.f;
-      }
+        for (int e = 0; e < 16; ++e)
+          acc[bi][bj][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[bi][bj][e], sc, -off));
+    } else {
+      const float coef = live ? gw * ep.S[t] : 0.f;
+      const float lse2 = live ? ep.lse[t] * kLog2e : 0.f;
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float q = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[bi][bj][e], sc, -lse2));
+          acc[bi][bj][e] = live ? coef * q : 0.f;
+        }
+    }
   }
   if ((ti.tm + 1) * BM > ep.V) {  // last vocabulary tile: rows past V carry no gradient
 #pragma unroll
@@ -816,10 +834,20 @@ __global__ __launch_bounds__(kFusedThreads, 1) void recompute_gemm_kernel(Operan
         for (int e = 0; e < 16; ++e)
           if (v_wave + bi * 32 + 8 * (e >> 2) + 4 * h + (e & 3) >= ep.V) acc[bi][bj][e] = 0.f;
   }
-  // Teacher entries: G -= gw * p at (t, i_{t,k}) (masked rows have none).
+  // Teacher entries: G -= gw * p at (t, i_{t,k}) (masked rows have none);
+  // bf16: |gw| p off the magnitude, then the sign of gw.
+  const float gp = kLogScale ? fabsf(gw) : gw;
   wh.for_each(ep.hits, [&](int q, int owner, int, int, float p) {
-    acc_add(acc, q, lane == owner ? -gw * p : 0.f);
+    acc_add(acc, q, lane == owner ? -gp * p : 0.f);
   });
+  if (kLogScale && gw < 0.f) {  // uniform: a negative incoming gradient
+#pragma unroll
+    for (int bj = 0; bj < NBJ; ++bj)
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[bi][bj][e] = -acc[bi][bj][e];
+  }
 
   T* G = static_cast<T*>(ep.G);
   // --- G^T[v][n] (fp32 only: the bf16 dW GEMM reads G itself k-major): for
