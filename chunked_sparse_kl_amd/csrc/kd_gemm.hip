@@ -727,7 +727,14 @@ __global__ __launch_bounds__(kFusedThreads, 1) void fwd_gemm_kernel(Operand A, O
     for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
       for (int e = 0; e < 16; e += 2) mx = max3f(mx, acc[bi][bj][e], acc[bi][bj][e + 1]);
-    mx = max3f(mx, __shfl_xor(mx, 32, 64), mx);
+    {
+      // the other half-wavefront's value (lane i ^ 32) by a register swap of
+      // the halves: {own, partner} for lanes 0-31, {partner, own} above
+      const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, mx),
+                                                      __builtin_bit_cast(unsigned, mx), false, false);
+      const unsigned r0 = r[0], r1 = r[1];  // (a bit_cast of a vector element would read element 0)
+      mx = max3f(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1), mx);
+    }
     float sm = 0.f;
     const float sc = kLog2e * ep.inv_tau;
     if (mx != kNegInf) {
@@ -737,7 +744,12 @@ __global__ __launch_bounds__(kFusedThreads, 1) void fwd_gemm_kernel(Operand A, O
 #pragma unroll
         for (int e = 0; e < 16; ++e) sm += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[bi][bj][e], sc, -mxs));
     }
-    sm += __shfl_xor(sm, 32, 64);
+    {
+      const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, sm),
+                                                      __builtin_bit_cast(unsigned, sm), false, false);
+      const unsigned r0 = r[0], r1 = r[1];
+      sm = __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+    }
     tmax[bj] = mx * ep.inv_tau;
     tsum[bj] = sm;
   }

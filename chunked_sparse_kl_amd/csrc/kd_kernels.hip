@@ -12,16 +12,46 @@ namespace {
 
 constexpr float kNegInf = -__builtin_inff();
 
+// Butterfly sum / max over the 64 lanes, every lane ending with the result,
+// through register-only cross-lane moves instead of the LDS crossbar: quad
+// permutes for partners i ^ 1 and i ^ 2, then the mirrored lane of the other
+// quad of each 8 (row_half_mirror) and of the other 8 of each 16
+// (row_mirror), then swaps of 16-lane rows and of 32-lane halves.  After each
+// step every lane of a group holds the same value, so the partner taken from
+// the other group has the value of lane i ^ o: the result is that of the xor
+// butterfly (v op= v[i ^ o], o = 1 .. 32) bit for bit.
+template <class Op>
+__device__ inline float wave_reduce(float v, Op op) {
+  auto dpp = [](float x, int ctrl) {
+    switch (ctrl) {  // the control word must be a constant
+      case 0xB1: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+      case 0x4E: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+      case 0x141: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
+      default: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
+    }
+  };
+  v = op(v, dpp(v, 0xB1));   // quad_perm [1, 0, 3, 2]: lane i ^ 1
+  v = op(v, dpp(v, 0x4E));   // quad_perm [2, 3, 0, 1]: lane i ^ 2
+  v = op(v, dpp(v, 0x141));  // row_half_mirror: the other quad of the 8
+  v = op(v, dpp(v, 0x140));  // row_mirror: the other 8 of the 16
+  // (the swaps' results are copied to scalars first: a bit_cast applied to a
+  // vector element reads element 0 with this compiler)
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);  // rows 0 <-> 1, 2 <-> 3
+  const unsigned a16 = r16[0], b16 = r16[1];
+  v = op(__builtin_bit_cast(float, a16), __builtin_bit_cast(float, b16));
+  const unsigned w = __builtin_bit_cast(unsigned, v);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);  // halves
+  const unsigned a32 = r32[0], b32 = r32[1];
+  return op(__builtin_bit_cast(float, a32), __builtin_bit_cast(float, b32));
+}
+
 __device__ inline float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  return wave_reduce(v, [](float a, float b) { return a + b; });
 }
 
 __device__ inline float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  return wave_reduce(v, [](float a, float b) { return fmaxf(a, b); });
 }
 
 // Merge of two (max, sum of exp(x - max)) pairs.
@@ -134,6 +164,56 @@ __device__ inline void resolve_repeated_ids(const int* ids, int K, int V, float*
   }
 }
 
+// The same for a row whose K <= 128 entries sit in registers: entry k = lane
+// in (v0, p0), entry 64 + lane in (v1, p1); slots past K hold id -1.  The
+// table (kDupSlots ids) only detects a repeat: an insertion that finds its
+// own id already there.  Rows with one then take the pairwise pass in k order.
+__device__ inline void resolve_repeated_ids_regs(int v0, int v1, int V, float& p0, float& p1, int* t_id) {
+  const int lane = threadIdx.x & 63;
+  for (int i = lane; i < kDupSlots; i += 64) t_id[i] = -1;
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  bool dup = false;
+  auto insert = [&](int v) {
+    if (v < 0 || v >= V) return;
+    int h = (int)(((unsigned)v * 2654435761u) >> 24);
+    for (;;) {
+      const int old = atomicCAS(&t_id[h], -1, v);
+      if (old == -1) break;
+      if (old == v) {
+        dup = true;
+        break;
+      }
+      h = (h + 1) & (kDupSlots - 1);
+    }
+  };
+  insert(v0);
+  insert(v1);
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // the table is cleared for the next row after this
+  if (!__any(dup)) return;
+  float np[2] = {p0, p1};
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int v = c ? v1 : v0, k = 64 * c + lane;
+    int f = k, n_same = 0;
+    float sum = 0.f;
+#pragma unroll
+    for (int cq = 0; cq < 2; ++cq) {
+      const int wv = cq ? v1 : v0;
+      const float pv = cq ? p1 : p0;
+      for (int u = 0; u < 64; ++u) {
+        if (__builtin_amdgcn_readlane(wv, u) == v) {
+          ++n_same;
+          f = min(f, 64 * cq + u);
+          sum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pv), u));
+        }
+      }
+    }
+    if (v >= 0 && v < V && n_same > 1) np[c] = f == k ? sum : 0.f;
+  }
+  p0 = np[0];
+  p1 = np[1];
+}
+
 // One workgroup (4 wavefronts) per 64-row block.  Each wavefront takes one row
 // at a time: renormalises the teacher's K log-values (the offline top-K cache
 // of the blog's "Two systems changes"), computes p = exp(l), S = sum p and
@@ -160,6 +240,85 @@ __global__ __launch_bounds__(256) void teacher_bucket_kernel(
 
   int live_rows = 0;
   bool bad = false;
+  // K <= 128: the 16 rows of a wavefront are loaded into registers at once
+  // (entries lane and 64 + lane of each) and stay there until placement, so
+  // the rows' loads overlap instead of running one after another.
+  constexpr int kRows = ROW_BLOCK / 4;
+  const bool regs = K <= 128;
+  int rv0[kRows], rv1[kRows];
+  float rp0[kRows], rp1[kRows];
+  if (regs) {
+    bool live[kRows];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      const int row = row_lo + wave + 4 * r;
+      const bool in = row < row_hi;
+      const long long base = (long long)row * K;
+      rv0[r] = in && lane < K ? idx[base + lane] : -1;
+      rv1[r] = in && lane + 64 < K ? idx[base + 64 + lane] : -1;
+      rp0[r] = in && lane < K ? logp[base + lane] : 0.f;
+      rp1[r] = in && lane + 64 < K ? logp[base + 64 + lane] : 0.f;
+      live[r] = in && (mask == nullptr || mask[row] != 0);
+    }
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      const int row = row_lo + wave + 4 * r;
+      if (row >= row_hi) continue;
+      const long long base = (long long)row * K;
+      if (!live[r]) {
+        if (lane < K) p[base + lane] = 0.f;
+        if (lane + 64 < K) p[base + 64 + lane] = 0.f;
+        if (lane == 0) {
+          S[row] = 0.f;
+          E[row] = 0.f;
+        }
+        rv0[r] = rv1[r] = -1;  // nothing to place
+        continue;
+      }
+      ++live_rows;
+      // the same arithmetic, in the same order, as the general path below
+      const float x0 = rv0[r] < 0 ? kNegInf : rp0[r] * inv_tau;
+      const float x1 = rv1[r] < 0 ? kNegInf : rp1[r] * inv_tau;
+      float mx = kNegInf;
+      if (lane < K) mx = fmaxf(mx, x0);
+      if (lane + 64 < K) mx = fmaxf(mx, x1);
+      mx = wave_max(mx);
+      float se = 0.f;
+      if (lane < K) se += expf(x0 - mx);
+      if (lane + 64 < K) se += expf(x1 - mx);
+      se = wave_sum(se);
+      const float lam = mx + logf(se);
+      float sp = 0.f, e = 0.f, p0 = 0.f, p1 = 0.f;
+      if (lane < K) {
+        const float l = x0 - lam;
+        p0 = expf(l);
+        sp += p0;
+        e += p0 > 0.f ? p0 * l : 0.f;
+      }
+      if (lane + 64 < K) {
+        const float l = x1 - lam;
+        p1 = expf(l);
+        sp += p1;
+        e += p1 > 0.f ? p1 * l : 0.f;
+      }
+      const int v0 = rv0[r], v1 = rv1[r];
+      if (v0 >= 0 && v0 < V) atomicAdd(&cnt[v0 / TILE_V], 1);
+      else if (v0 >= V) bad = true;
+      if (v1 >= 0 && v1 < V) atomicAdd(&cnt[v1 / TILE_V], 1);
+      else if (v1 >= V) bad = true;
+      sp = wave_sum(sp);
+      e = wave_sum(e);
+      if (lane == 0) {
+        S[row] = sp;
+        E[row] = e;
+      }
+      resolve_repeated_ids_regs(v0, v1, V, p0, p1, dup_tab + wave * 3 * kDupSlots);
+      if (lane < K) p[base + lane] = p0;
+      if (lane + 64 < K) p[base + 64 + lane] = p1;
+      rp0[r] = p0;
+      rp1[r] = p1;
+    }
+  } else
   for (int row = row_lo + wave; row < row_hi; row += 4) {
     const long long base = (long long)row * K;
     if (mask != nullptr && mask[row] == 0) {
@@ -234,7 +393,29 @@ __global__ __launch_bounds__(256) void teacher_bucket_kernel(
   }
   __syncthreads();
 
-  // Placement: p is re-read from memory this workgroup wrote before the barrier.
+  // Placement.  Register path: ids and p (after the repeated-id pass) from
+  // registers; rows past the block end and masked rows hold id -1.
+  if (regs) {
+    auto place = [&](int row, int k, int v, float pk) {
+      if (v >= 0 && v < V) {
+        const int pos = atomicAdd(&cnt[v / TILE_V], 1);
+        Hit h;
+        h.row = row;
+        h.k = k;
+        h.v = v;
+        h.p = pk;
+        hits[hit_base + pos] = h;
+      }
+    };
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      const int row = row_lo + wave + 4 * r;
+      place(row, lane, rv0[r], rp0[r]);
+      place(row, 64 + lane, rv1[r], rp1[r]);
+    }
+    return;
+  }
+  // General path: p is re-read from memory this workgroup wrote before the barrier.
   for (int row = row_lo + wave; row < row_hi; row += 4) {
     if (mask != nullptr && mask[row] == 0) continue;
     const long long base = (long long)row * K;

@@ -90,6 +90,35 @@ def test_duplicates_neginf_and_shifted_teacher():
     check_full(inp, gpu, "bf16", grad=0.37)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_register_and_general_teacher_paths_agree(dtype):
+    """Rows of K <= 128 entries are prepared from registers, longer rows by the
+    general loop.  The same rows at K = 100 and padded to K = 140 (ids -1 at
+    the end, garbage log-values under them) take one path each and give
+    bit-identical results: padding adds exact zeros, repeated ids are summed
+    in k order on both paths."""
+    inp = synth.make_custom(700, 128, 1500, 100, dtype, "random5", "uniform", seed=31)
+    idx = inp["idx"].numpy()
+    rng = np.random.default_rng(31)
+    for t in range(0, 700, 5):
+        src = rng.choice(100, size=6, replace=False)
+        dst = rng.choice(100, size=6, replace=False)
+        idx[t, dst] = idx[t, src]
+    idx[2, 60:70] = idx[2, 0]                      # across the 64-entry boundary
+    inp["idx"] = torch.from_numpy(idx)
+    padded = dict(inp)
+    padded["idx"] = torch.cat([inp["idx"], torch.full((700, 40), -1, dtype=torch.int32)], 1).contiguous()
+    padded["logp"] = torch.cat([inp["logp"], torch.full((700, 40), 3.0)], 1).contiguous()
+    a = run_gpu(inp, chunk=192, grad=0.9)
+    b = run_gpu(padded, chunk=192, grad=0.9)
+    assert a["loss"] == b["loss"]
+    for k in ("lse", "row_kl", "dH", "dW"):
+        assert np.array_equal(a[k], b[k]), k
+    live = inp["mask"].numpy() != 0
+    assert np.array_equal(a["g"][live], b["g"][live][:, :100])
+    check_full(inp, a, dtype, grad=0.9)
+
+
 def test_clustered_ids_overflow_tiles():
     # every teacher id of every row inside one 256-wide vocabulary tile
     inp = synth.make_custom(256, 64, 2048, 100, "bf16", "ones", "uniform", seed=8)
