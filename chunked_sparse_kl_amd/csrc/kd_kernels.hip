@@ -434,15 +434,16 @@ __global__ __launch_bounds__(256) void teacher_bucket_kernel(
   }
 }
 
-// 32 chunk rows per workgroup, 8 slices per row: slice s merges the
-// per-vocabulary-tile (max, sum-exp) partials j = s, s+8, ... and the teacher
-// terms k = s, s+8, ...; the slices are then combined in slice order.  The
+// 32 chunk rows per workgroup, 32 slices per row (1024 threads, so enough
+// loads are in flight): slice s merges the per-vocabulary-tile (max, sum-exp)
+// partials j = s, s+32, ... and the teacher terms k = s, s+32, ...; the slices
+// are then combined in slice order.  The
 // merge order depends only on the number of vocabulary tiles, so LSE and KL do
 // not depend on the chunk size.  The partials are of the softened logits
 // z / tau, so LSE_t is that of z / tau, and
 // KL_t = tau^2 (E_t - sum_k p_k g_k / tau + S_t * LSE_t).
-constexpr int kKlRows = 32, kKlSlices = 8;
-__global__ __launch_bounds__(256) void lse_kl_kernel(const float2* __restrict__ part, int ld_part,
+constexpr int kKlRows = 32, kKlSlices = 32;
+__global__ __launch_bounds__(kKlRows * kKlSlices) void lse_kl_kernel(const float2* __restrict__ part, int ld_part,
                                                      int n_vt, int c0, int rows,
                                                      const float* __restrict__ p,
                                                      const float* __restrict__ g,
@@ -624,7 +625,7 @@ void launch_teacher_bucket(const float* logp, const int* idx, const uint8_t* mas
 void launch_lse_kl(const float2* part, int ld_part, int n_vt, int c0, int rows, const float* p,
                    const float* g, const float* S, const float* E, const uint8_t* mask, int K,
                    float tau, float* lse, float* row_kl, hipStream_t s) {
-  lse_kl_kernel<<<(rows + kKlRows - 1) / kKlRows, 256, 0, s>>>(part, ld_part, n_vt, c0, rows, p, g,
+  lse_kl_kernel<<<(rows + kKlRows - 1) / kKlRows, kKlRows * kKlSlices, 0, s>>>(part, ld_part, n_vt, c0, rows, p, g,
                                                                 S, E, mask, K, tau, lse, row_kl);
 }
 
