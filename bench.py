@@ -43,9 +43,15 @@ def kernel_traffic(kernel: str, workload: str = None):
     rec = json.load(open(path))
     if workload is not None and rec.get("workload") != workload:
         return None
-    src = open(os.path.join(ROOT, "chunked_sparse_kl_amd", "csrc", rec["source_file"]), "rb").read()
-    if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
-        return None
+    # the kernel source, and (where the record names it) the host code that
+    # decides how many rows one launch covers, must be the ones measured
+    for f, h in ((rec["source_file"], rec["source_sha256"]),
+                 (rec.get("driver_file"), rec.get("driver_sha256"))):
+        if f is None:
+            continue
+        src = open(os.path.join(ROOT, "chunked_sparse_kl_amd", "csrc", f), "rb").read()
+        if hashlib.sha256(src).hexdigest() != h:
+            return None
     return rec["hbm_bytes_per_launch"]
 
 

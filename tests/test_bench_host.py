@@ -39,13 +39,16 @@ def test_roofline_of_a_memory_bound_dominant_kernel():
 
 
 def test_committed_traffic_records_are_used_only_for_their_source_and_workload():
-    # every committed record names its kernel, workload and the source it was taken on;
-    # it is reported only while that source is unchanged, and only for that workload
+    # every committed record names its kernel, workload, the kernel source and the host
+    # code (rows per launch) it was taken on; it is reported only while both are
+    # unchanged, and only for that workload
     for k in ("fwd_gemm", "recompute_gemm", "dh_gemm", "dw_gemm"):
         rec = json.load(open(os.path.join(ROOT, "profiles", f"traffic_{k}.json")))
         assert rec["kernel"] == k and rec["hbm_bytes_per_launch"] > 0
-        src = open(os.path.join(ROOT, "chunked_sparse_kl_amd", "csrc", rec["source_file"]), "rb").read()
-        same = hashlib.sha256(src).hexdigest() == rec["source_sha256"]
+        same = True
+        for f, h in ((rec["source_file"], rec["source_sha256"]), (rec["driver_file"], rec["driver_sha256"])):
+            src = open(os.path.join(ROOT, "chunked_sparse_kl_amd", "csrc", f), "rb").read()
+            same = same and hashlib.sha256(src).hexdigest() == h
         assert bench.kernel_traffic(k, rec["workload"]) == (rec["hbm_bytes_per_launch"] if same else None)
         assert bench.kernel_traffic(k, "another workload chunk 64") is None
 
@@ -65,6 +68,15 @@ def test_traffic_record_of_another_source_is_ignored(tmp_path, monkeypatch):
     (prof / "traffic_x_gemm.json").write_text(json.dumps(rec))
     assert bench.kernel_traffic("x_gemm", "w chunk 8") == 5
     assert bench.kernel_traffic("missing_gemm", "w chunk 8") is None
+    # a record that also names the host code choosing the rows per launch
+    (csrc / "api.cpp").write_text("// launches per pair of chunks\n")
+    rec["driver_file"] = "api.cpp"
+    rec["driver_sha256"] = hashlib.sha256(b"// launches per chunk\n").hexdigest()
+    (prof / "traffic_x_gemm.json").write_text(json.dumps(rec))
+    assert bench.kernel_traffic("x_gemm", "w chunk 8") is None
+    rec["driver_sha256"] = hashlib.sha256(b"// launches per pair of chunks\n").hexdigest()
+    (prof / "traffic_x_gemm.json").write_text(json.dumps(rec))
+    assert bench.kernel_traffic("x_gemm", "w chunk 8") == 5
 
 
 def test_more_than_one_gpu_is_refused():
