@@ -67,9 +67,10 @@ __global__ void fill_i32_kernel(int* p, long long count, int value) {
   for (; i < count; i += stride) p[i] = value;
 }
 
-// Exclusive scan over the 256 threads of a workgroup (fixed order); *total
-// receives the sum.  sh: 4 ints of LDS.
-__device__ inline int block256_exclusive_scan(int v, int* sh, int* total) {
+// Exclusive scan over the kWaves wavefronts of a workgroup (fixed order);
+// *total receives the sum.  sh: kWaves ints of LDS.
+template <int kWaves>
+__device__ inline int block_exclusive_scan(int v, int* sh, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int incl = v;
 #pragma unroll
@@ -79,69 +80,29 @@ __device__ inline int block256_exclusive_scan(int v, int* sh, int* total) {
   }
   if (lane == 63) sh[wave] = incl;
   __syncthreads();
-  int base = 0;
-  for (int w = 0; w < wave; ++w) base += sh[w];
-  *total = sh[0] + sh[1] + sh[2] + sh[3];
+  int base = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    base += w < wave ? sh[w] : 0;
+    all += sh[w];
+  }
+  *total = all;
   __syncthreads();
   return base + incl - v;
 }
 
-// Per-wavefront table that finds the ids a row repeats: open addressing over
-// kDupSlots slots of (id, smallest k, largest k); rows with K <= kDupSlots / 2
-// use it (load factor <= 1/2), longer rows compare every pair of entries.
+// Slots of the per-wavefront table that detects repeated ids in a row of at
+// most 128 entries (load factor <= 1/2).
 constexpr int kDupSlots = 256;
 
-// For one row (ids[0..K), p[0..K) as stored, p_of(k) recomputes p bitwise):
-// where an id occurs more than once, p at its first occurrence becomes the
-// sum of its occurrences' p in k order and p at the others becomes 0.
-// Ids < 0 or >= V are left alone.  Called by a whole wavefront.
+// For one row of more than 128 entries (ids[0..K), p[0..K) as stored, p_of(k)
+// recomputes p bitwise): where an id occurs more than once, p at its first
+// occurrence becomes the sum of its occurrences' p in k order and p at the
+// others becomes 0.  Every entry is compared with every other one.  Ids < 0
+// or >= V are left alone.  Called by a whole wavefront.
 template <class PK>
-__device__ inline void resolve_repeated_ids(const int* ids, int K, int V, float* p, int* tab, PK&& p_of) {
+__device__ inline void resolve_repeated_ids(const int* ids, int K, int V, float* p, PK&& p_of) {
   const int lane = threadIdx.x & 63;
-  constexpr int kMaxChunks = kDupSlots / 2 / 64;
-  int first[kMaxChunks], last[kMaxChunks];
-  if (K <= kDupSlots / 2) {
-    int* const t_id = tab;
-    int* const t_min = tab + kDupSlots;
-    int* const t_max = tab + 2 * kDupSlots;
-    for (int i = lane; i < kDupSlots; i += 64) {
-      t_id[i] = -1;
-      t_min[i] = 0x7fffffff;
-      t_max[i] = -1;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    int slot[kMaxChunks];
-#pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) {
-      const int k = 64 * c + lane;
-      slot[c] = -1;
-      const int v = k < K ? ids[k] : -1;
-      if (v >= 0 && v < V) {
-        int h = (int)(((unsigned)v * 2654435761u) >> 24);  // Fibonacci hash to 8 bits
-        for (;;) {
-          const int old = atomicCAS(&t_id[h], -1, v);
-          if (old == -1 || old == v) break;
-          h = (h + 1) & (kDupSlots - 1);
-        }
-        atomicMin(&t_min[h], k);
-        atomicMax(&t_max[h], k);
-        slot[c] = h;
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-#pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) {
-      first[c] = slot[c] >= 0 ? t_min[slot[c]] : 0;
-      last[c] = slot[c] >= 0 ? t_max[slot[c]] : 0;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // the table is cleared for the next row after this
-    bool any_dup = false;
-#pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) any_dup |= first[c] != last[c];
-    if (!__any(any_dup)) return;  // the common case: no repeated id in the row
-  }
-  // first / last occurrence by comparing with every entry (long rows, or the
-  // rows of the table path that repeat an id), then the sums in k order
   for (int k0 = 0; k0 < K; k0 += 64) {
     const int k = k0 + lane;
     const int v = k < K ? ids[k] : -1;
@@ -165,9 +126,9 @@ __device__ inline void resolve_repeated_ids(const int* ids, int K, int V, float*
 }
 
 // The same for a row whose K <= 128 entries sit in registers: entry k = lane
-// in (v0, p0), entry 64 + lane in (v1, p1); slots past K hold id -1.  The
-// table (kDupSlots ids) only detects a repeat: an insertion that finds its
-// own id already there.  Rows with one then take the pairwise pass in k order.
+// in (v0, p0), entry 64 + lane in (v1, p1); slots past K hold id -1.  A table
+// of kDupSlots ids in LDS detects a repeat (an insertion that finds its own id
+// already there); only rows with one take the pairwise pass in k order.
 __device__ inline void resolve_repeated_ids_regs(int v0, int v1, int V, float& p0, float& p1, int* t_id) {
   const int lane = threadIdx.x & 63;
   for (int i = lane; i < kDupSlots; i += 64) t_id[i] = -1;
@@ -214,8 +175,8 @@ __device__ inline void resolve_repeated_ids_regs(int v0, int v1, int V, float& p
   p1 = np[1];
 }
 
-// One workgroup (4 wavefronts) per 64-row block.  Each wavefront takes one row
-// at a time: renormalises the teacher's K log-values (the offline top-K cache
+// One workgroup (kBucketWaves wavefronts) per 64-row block.  Each wavefront
+// takes one row at a time: renormalises the teacher's K log-values (the offline top-K cache
 // of the blog's "Two systems changes"), computes p = exp(l), S = sum p and
 // E = sum p*l (0*log 0 := 0), stores p (for an id the row repeats: the sum
 // of its occurrences' p at the first one, 0 at the others), and counts the
@@ -224,26 +185,29 @@ __device__ inline void resolve_repeated_ids_regs(int v0, int v1, int V, float& p
 // entirely; ids >= V set the range flag and are dropped; ids < 0 are padding
 // (probability 0, outside the renormalisation).  The log-values are divided
 // by the temperature (inv_tau = 1 / tau) before the renormalisation.
-__global__ __launch_bounds__(256) void teacher_bucket_kernel(
+constexpr int kBucketWaves = 8;
+constexpr int kBucketThreads = 64 * kBucketWaves;
+__global__ __launch_bounds__(kBucketThreads) void teacher_bucket_kernel(
     const float* __restrict__ logp, const int* __restrict__ idx, const uint8_t* __restrict__ mask,
     int n, int K, int V, int n_vt, float inv_tau, float* __restrict__ p, float* __restrict__ S,
     float* __restrict__ E, int* __restrict__ hit_off, Hit* __restrict__ hits, Ctrl* ctrl) {
   extern __shared__ int cnt[];  // n_vt + 1 counters (then cursors), then the repeated-id tables
-  __shared__ int sh[4];
+  __shared__ int sh[kBucketWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rb = blockIdx.x;
   const int row_lo = rb * ROW_BLOCK, row_hi = min(row_lo + ROW_BLOCK, n);
   const int n_ct = n_vt + 1;
-  int* const dup_tab = cnt + n_ct;  // 4 wavefronts x 3 x kDupSlots
-  for (int j = tid; j < n_ct; j += 256) cnt[j] = 0;
+  int* const dup_tab = cnt + n_ct;  // kBucketWaves x kDupSlots
+  for (int j = tid; j < n_ct; j += kBucketThreads) cnt[j] = 0;
   __syncthreads();
 
   int live_rows = 0;
   bool bad = false;
-  // K <= 128: the 16 rows of a wavefront are loaded into registers at once
-  // (entries lane and 64 + lane of each) and stay there until placement, so
-  // the rows' loads overlap instead of running one after another.
-  constexpr int kRows = ROW_BLOCK / 4;
+  // K <= 128: the rows of a wavefront (kRows of them) are loaded into
+  // registers at once (entries lane and 64 + lane of each) and stay there
+  // until placement, so the rows' loads overlap instead of running one after
+  // another.
+  constexpr int kRows = ROW_BLOCK / kBucketWaves;
   const bool regs = K <= 128;
   int rv0[kRows], rv1[kRows];
   float rp0[kRows], rp1[kRows];
@@ -251,7 +215,7 @@ __global__ __launch_bounds__(256) void teacher_bucket_kernel(
     bool live[kRows];
 #pragma unroll
     for (int r = 0; r < kRows; ++r) {
-      const int row = row_lo + wave + 4 * r;
+      const int row = row_lo + wave + kBucketWaves * r;
       const bool in = row < row_hi;
       const long long base = (long long)row * K;
       rv0[r] = in && lane < K ? idx[base + lane] : -1;
@@ -262,7 +226,7 @@ __global__ __launch_bounds__(256) void teacher_bucket_kernel(
     }
 #pragma unroll
     for (int r = 0; r < kRows; ++r) {
-      const int row = row_lo + wave + 4 * r;
+      const int row = row_lo + wave + kBucketWaves * r;
       if (row >= row_hi) continue;
       const long long base = (long long)row * K;
       if (!live[r]) {
@@ -312,14 +276,14 @@ __global__ __launch_bounds__(256) void teacher_bucket_kernel(
         S[row] = sp;
         E[row] = e;
       }
-      resolve_repeated_ids_regs(v0, v1, V, p0, p1, dup_tab + wave * 3 * kDupSlots);
+      resolve_repeated_ids_regs(v0, v1, V, p0, p1, dup_tab + wave * kDupSlots);
       if (lane < K) p[base + lane] = p0;
       if (lane + 64 < K) p[base + 64 + lane] = p1;
       rp0[r] = p0;
       rp1[r] = p1;
     }
   } else
-  for (int row = row_lo + wave; row < row_hi; row += 4) {
+  for (int row = row_lo + wave; row < row_hi; row += kBucketWaves) {
     const long long base = (long long)row * K;
     if (mask != nullptr && mask[row] == 0) {
       for (int k = lane; k < K; k += 64) p[base + k] = 0.f;
@@ -367,7 +331,7 @@ __global__ __launch_bounds__(256) void teacher_bucket_kernel(
     // of distinct (row, id) touch distinct accumulators and the result no
     // longer depends on the bucket order.  The forward's sum of p * g is the
     // same sum (repeated ids share one logit g); S and E above use every p.
-    resolve_repeated_ids(idx + base, K, V, p + base, dup_tab + wave * 3 * kDupSlots, [&](int k) {
+    resolve_repeated_ids(idx + base, K, V, p + base, [&](int k) {
       return expf(a_of(k) - lam);  // bitwise the p stored above
     });
   }
@@ -377,12 +341,12 @@ __global__ __launch_bounds__(256) void teacher_bucket_kernel(
 
   // Exclusive scan of the n_vt + 1 counters (the last one is 0, so it ends as
   // the block's total); thread t owns a contiguous run of them.
-  const int per = (n_ct + 255) / 256;
+  const int per = (n_ct + kBucketThreads - 1) / kBucketThreads;
   const int j0 = min(tid * per, n_ct), j1 = min(j0 + per, n_ct);
   int run = 0;
   for (int j = j0; j < j1; ++j) run += cnt[j];
   int total;
-  run = block256_exclusive_scan(run, sh, &total);
+  run = block_exclusive_scan<kBucketWaves>(run, sh, &total);
   const int hit_base = rb * ROW_BLOCK * K;
   int* off = hit_off + (long long)rb * n_ct;
   for (int j = j0; j < j1; ++j) {
@@ -409,14 +373,14 @@ __global__ __launch_bounds__(256) void teacher_bucket_kernel(
     };
 #pragma unroll
     for (int r = 0; r < kRows; ++r) {
-      const int row = row_lo + wave + 4 * r;
+      const int row = row_lo + wave + kBucketWaves * r;
       place(row, lane, rv0[r], rp0[r]);
       place(row, 64 + lane, rv1[r], rp1[r]);
     }
     return;
   }
   // General path: p is re-read from memory this workgroup wrote before the barrier.
-  for (int row = row_lo + wave; row < row_hi; row += 4) {
+  for (int row = row_lo + wave; row < row_hi; row += kBucketWaves) {
     if (mask != nullptr && mask[row] == 0) continue;
     const long long base = (long long)row * K;
     for (int k = lane; k < K; k += 64) {
@@ -617,8 +581,8 @@ void launch_teacher_bucket(const float* logp, const int* idx, const uint8_t* mas
                            Hit* hits, Ctrl* ctrl, hipStream_t s) {
   const int n_vt = (V + TILE_V - 1) / TILE_V;
   const int n_rb = (n + ROW_BLOCK - 1) / ROW_BLOCK;
-  const size_t lds = (size_t(n_vt + 1) + 4 * 3 * kDupSlots) * sizeof(int);
-  teacher_bucket_kernel<<<n_rb, 256, lds, s>>>(logp, idx, mask, n, K, V, n_vt, inv_tau, p, S, E,
+  const size_t lds = (size_t(n_vt + 1) + kBucketWaves * kDupSlots) * sizeof(int);
+  teacher_bucket_kernel<<<n_rb, kBucketThreads, lds, s>>>(logp, idx, mask, n, K, V, n_vt, inv_tau, p, S, E,
                                                hit_off, hits, ctrl);
 }
 
