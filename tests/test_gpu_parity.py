@@ -119,6 +119,21 @@ def test_register_and_general_teacher_paths_agree(dtype):
     check_full(inp, a, dtype, grad=0.9)
 
 
+@pytest.mark.parametrize("K", [63, 64, 65, 127, 128, 129])
+def test_teacher_row_lengths_at_the_lane_boundaries(K):
+    """K around one and two 64-lane rows of entries: 64 and 128 fill the
+    registers of the register path exactly, 65 puts one entry in the second
+    register, 129 takes the general path.  Rows repeat ids across the two
+    registers."""
+    inp = synth.make_custom(200, 64, 2000, K, "bf16", "random5", "uniform", seed=32 + K)
+    idx = inp["idx"].numpy()
+    idx[1, K - 1] = idx[1, 0]
+    idx[3, K // 2:K // 2 + 3] = idx[3, 1]
+    inp["idx"] = torch.from_numpy(idx)
+    inp["mask"][[1, 3]] = 1
+    check_full(inp, run_gpu(inp, chunk=128, grad=1.3), "bf16", grad=1.3)
+
+
 def test_clustered_ids_overflow_tiles():
     # every teacher id of every row inside one 256-wide vocabulary tile
     inp = synth.make_custom(256, 64, 2048, 100, "bf16", "ones", "uniform", seed=8)
