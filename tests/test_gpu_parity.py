@@ -134,6 +134,28 @@ def test_teacher_row_lengths_at_the_lane_boundaries(K):
     check_full(inp, run_gpu(inp, chunk=128, grad=1.3), "bf16", grad=1.3)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_negative_incoming_gradient(dtype):
+    """grad_loss < 0: the gradients are the negated ones of |grad_loss|.  bf16 G
+    carries the sign of the row factor apart from its magnitude, so G itself is
+    exactly negated; the bf16 MFMA's fp32 accumulation is not exactly symmetric
+    under negation of an operand (about 8% of dW's fp32 entries move by an
+    ulp, measured), so dH and dW are compared bit for bit in fp32 and to a
+    relative 1e-6 in bf16."""
+    inp = synth.make_custom(400, 96, 1300, 24, dtype, "random5", "uniform", seed=33)
+    idx = inp["idx"].numpy()
+    idx[5, 3] = idx[5, 0]                          # a repeated id
+    inp["idx"] = torch.from_numpy(idx)
+    inp["mask"][5] = 1
+    pos = run_gpu(inp, chunk=192, grad=0.8)
+    neg = run_gpu(inp, chunk=192, grad=-0.8)
+    assert neg["loss"] == pos["loss"]
+    if dtype == "f32":
+        assert np.array_equal(neg["dH"], -pos["dH"]) and np.array_equal(neg["dW"], -pos["dW"])
+    assert rel_fro(neg["dH"], -pos["dH"]) <= 1e-6 and rel_fro(neg["dW"], -pos["dW"]) <= 1e-6
+    check_full(inp, neg, dtype, grad=-0.8)
+
+
 def test_clustered_ids_overflow_tiles():
     # every teacher id of every row inside one 256-wide vocabulary tile
     inp = synth.make_custom(256, 64, 2048, 100, "bf16", "ones", "uniform", seed=8)
