@@ -122,6 +122,27 @@ def test_variant_agrees_with_fused_at_the_4k_workload(name):
     assert rel_fro(got["dH"], fused["dH"]) <= 5e-3 and rel_fro(got["dW"], fused["dW"]) <= 5e-3
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_variant_random_configuration(seed):
+    """Seeded random sizes, chunks, masks and incoming gradients (bf16, the
+    variants' dtype), with padding entries; the oracle as the reference."""
+    rng = np.random.default_rng(7000 + seed)
+    n = int(rng.integers(1, 600))
+    d = int(rng.choice([8, 40, 64, 136, 256]))
+    K = int(rng.choice([1, 17, 64, 65, 100, 129]))
+    V = int(rng.integers(K + 1, 2500))
+    inp = synth.make_custom(n, d, V, K, "bf16", "random5" if n >= 20 else "ones", "uniform", seed=7100 + seed)
+    idx = inp["idx"].numpy()
+    for t in rng.choice(n, size=min(n, 6), replace=False):
+        idx[t, int(rng.integers(1, K + 1)):] = -1
+    inp["idx"] = torch.from_numpy(idx)
+    chunk = int(rng.choice([0, 64, 192, 256]))
+    grad = float(rng.uniform(0.3, 1.5)) * (-1.0 if seed % 3 == 1 else 1.0)
+    name = sorted(VARIANTS)[seed % 2]
+    print(f"[case] {name} n={n} d={d} V={V} K={K} chunk={chunk} grad={grad:.3f}", flush=True)
+    check_full(inp, run_variant(name, inp, chunk=chunk, grad=grad), "bf16", grad=grad)
+
+
 def test_fp32_inputs_are_refused():
     inp = to_device(synth.make_custom(64, 32, 300, 4, "f32", "ones", "uniform", seed=45))
     for name, (fwd, _) in VARIANTS.items():
