@@ -87,3 +87,34 @@ def test_rows_subset_and_bf16_upcast():
     np.testing.assert_array_equal(sub["logp"], full["logp"][rows])
     ref = Ht.double().numpy() @ Wt.double().numpy().T   # bf16 -> fp64 exact
     np.testing.assert_array_equal(full["z"], ref)
+
+
+def _bf16_words_case(rows: int, cols: int, seed: int) -> np.ndarray:
+    """bf16 bit patterns (uint16) of values a half-precision round trip
+    would change: magnitudes above 65504 (fp16 overflows) and below 2^-14
+    (fp16 subnormals, fewer mantissa bits), with full 7-bit mantissas."""
+    rng = np.random.default_rng(seed)
+    sign = rng.integers(0, 2, size=(rows, cols)).astype(np.uint16) << 15
+    big = rng.integers(127 + 16, 127 + 21, size=(rows, cols))       # 2^16 .. 2^20
+    small = rng.integers(127 - 22, 127 - 17, size=(rows, cols))     # 2^-22 .. 2^-18
+    expo = np.where(rng.random((rows, cols)) < 0.5, big, small).astype(np.uint16) << 7
+    mant = rng.integers(0, 128, size=(rows, cols)).astype(np.uint16)
+    return sign | expo | mant
+
+
+def _decode(words: np.ndarray) -> np.ndarray:
+    """Hand decode of bf16 words: the upper half of an fp32 word."""
+    return (words.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def test_bf16_upcast_outside_half_precision():
+    Hw, Ww = _bf16_words_case(6, 16, 11), _bf16_words_case(40, 16, 12)
+    Ht = torch.from_numpy(Hw.view(np.int16)).view(torch.bfloat16)
+    Wt = torch.from_numpy(Ww.view(np.int16)).view(torch.bfloat16)
+    assert not torch.equal(Ht.float().half().float(), Ht.float())   # the case exercises fp16's limits
+    assert np.array_equal(T.to_f64(Ht), _decode(Hw))
+    got = T.build_cache(Ht, Wt, 5)
+    ref = T.build_cache(_decode(Hw), _decode(Ww), 5)
+    assert np.isfinite(got["z"]).all()
+    np.testing.assert_array_equal(got["z"], _decode(Hw) @ _decode(Ww).T)
+    assert np.array_equal(got["ids"], ref["ids"]) and np.array_equal(got["logp"], ref["logp"])
