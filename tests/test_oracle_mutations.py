@@ -54,6 +54,21 @@ MUTATIONS = [
      "lse = np.log(np.exp(z - m).sum(axis=1, keepdims=True))"),
     ("bf16 upcast through half precision",
      "x = x.float()", "x = x.half().float()"),
+    ("zero-probability entries not set aside (0 * -inf)",
+     "terms = np.where(p > 0, p * (l - logq_ids), 0.0)", "terms = p * (l - logq_ids)"),
+    ("student not softened by the temperature in the forward",
+     "lse_b, logq = full_log_softmax(z / tau)", "lse_b, logq = full_log_softmax(z)"),
+    ("student not softened by the temperature in the backward",
+     "_, logq = full_log_softmax(z / tau)", "_, logq = full_log_softmax(z)"),
+    ("log-probability stored as the gathered logit",
+     "g_b[live] = np.where(pad[blk][live], np.nan, gather(z[live], ids_live))",
+     "g_b[live] = np.where(pad[blk][live], np.nan, gather(logq[live], ids_live))"),
+    ("teacher entries scattered into the wrong rows",
+     "r = np.repeat(np.arange(blk.size), idx.shape[1])", "r = np.tile(np.arange(blk.size), idx.shape[1])"),
+    ("masked rows kept in the gradient",
+     "live_rows = rows[mask[rows] != 0]", "live_rows = rows"),
+    ("gradient divided by all rows",
+     "nv = live_rows.size", "nv = rows.size"),
 ]
 
 
