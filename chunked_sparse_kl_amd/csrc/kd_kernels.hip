@@ -176,15 +176,16 @@ __device__ inline void resolve_repeated_ids_regs(int v0, int v1, int V, float& p
 }
 
 // One workgroup (kBucketWaves wavefronts) per 64-row block.  Each wavefront
-// takes one row at a time: renormalises the teacher's K log-values (the offline top-K cache
-// of the blog's "Two systems changes"), computes p = exp(l), S = sum p and
-// E = sum p*l (0*log 0 := 0), stores p (for an id the row repeats: the sum
-// of its occurrences' p at the first one, 0 at the others), and counts the
-// row's ids per vocabulary tile in LDS.  The counts are then scanned into this block's bucket offsets and every
-// entry is placed in its bucket with LDS cursors.  Masked rows are skipped
-// entirely; ids >= V set the range flag and are dropped; ids < 0 are padding
-// (probability 0, outside the renormalisation).  The log-values are divided
-// by the temperature (inv_tau = 1 / tau) before the renormalisation.
+// takes one row at a time: renormalises the teacher's K log-values (the
+// offline top-K cache of the blog's "Two systems changes"), computes
+// p = exp(l), S = sum p and E = sum p*l (0*log 0 := 0), stores p (for an id
+// the row repeats: the sum of its occurrences' p at the first one, 0 at the
+// others), and counts the row's ids per vocabulary tile in LDS.  The counts
+// are then scanned into this block's bucket offsets and every entry is placed
+// in its bucket with LDS cursors.  Masked rows are skipped entirely; ids >= V
+// set the range flag and are dropped; ids < 0 are padding (probability 0,
+// outside the renormalisation).  The log-values are divided by the
+// temperature (inv_tau = 1 / tau) before the renormalisation.
 constexpr int kBucketWaves = 8;
 constexpr int kBucketThreads = 64 * kBucketWaves;
 __global__ __launch_bounds__(kBucketThreads) void teacher_bucket_kernel(
