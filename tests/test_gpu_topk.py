@@ -130,3 +130,20 @@ def test_full_size_sampled_rows():
     rows = np.concatenate([[0, 8191, 8192, Ht.shape[0] - 1], rows])
     _check(Ht, Wt, 100, idx, logp, rows=rows, eps=2e-4)
     assert (np.diff(logp, axis=1) <= 1e-3).all()
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_configuration(seed):
+    """Seeded random rows, hidden sizes, vocabularies (ragged against the
+    256-wide tiles) and K, both dtypes, chunk chosen by the planner or given."""
+    rng = np.random.default_rng(8000 + seed)
+    dtype = "f32" if seed % 3 == 0 else "bf16"
+    n = int(rng.integers(1, 500))
+    d = int(rng.choice([8, 16, 40, 64, 136, 256]))
+    V = int(rng.integers(2, 6000))
+    K = int(min(V, rng.choice([1, 5, 24, 63, 64, 65, 100, 128, 129])))
+    chunk = int(rng.choice([0, 64, 256]))
+    print(f"[case] {dtype} n={n} d={d} V={V} K={K} chunk={chunk}", flush=True)
+    Ht, Wt = _inputs(n, d, V, dtype, 8100 + seed)
+    idx, logp = _run(Ht, Wt, K, chunk=chunk)
+    _check(Ht, Wt, K, idx, logp)
